@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the frame-aligned attention hot path on one MI355X.
+
+A step is one streaming chunk of the 1560-token, 40-head workload: the
+attention over (ring history in the 12-frame window, the 3-frame chunk, its
+3 source frames, the 1560-token reference) followed by the ring append.
+Steps walk the 20-chunk stream (chunk i of a step counter k is k mod 20, so a
+20-step run covers the warm-up chunks and the steady state); inputs of all 20
+chunks are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is useful TFLOP/s (4*head_dim FLOPs per
+visible query-key pair) over the timed steps; `roofline` is the attention
+kernel against the bf16 MFMA peak, timed with HIP events on the stream the
+kernel runs on; `cpu_baseline` is the CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "frame-aligned attn useful TFLOP/s + ms per streaming chunk, 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_stream1560_h40_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "frame_aligned_attention_amd", "csrc", "fa_attn_bf16.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_sha():
+        return None
+    return float(b.group(1))
+
+
+def build_stream_inputs(w, torch, W, B, H=None):
+    H = H or w.H
+    chunks = []
+    rows = w.C * w.T
+    r = W.ref_tensors(w, H=H)
+    dev = lambda x: torch.from_numpy(x).unsqueeze(0).to("cuda").to(torch.bfloat16).contiguous()
+    ref = {"k_ref": dev(r["k_ref"]), "v_ref": dev(r["v_ref"])}
+    ring = {n: torch.zeros((1, w.cache_frames * w.T, H, w.D), dtype=torch.bfloat16, device="cuda")
+            for n in ("k_ring", "v_ring")}
+    o = torch.empty((1, rows, H, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, H, rows), dtype=torch.float32, device="cuda")
+    for ch in range(w.chunks):
+        x = W.chunk_tensors(w, ch, H=H)
+        t = {n: dev(x[n]) for n in ("q_tgt", "k_tgt", "v_tgt", "k_src", "v_src")}
+        t.update(ref)
+        t.update(ring)
+        t["o_tgt"], t["lse_tgt"] = o, lse
+        chunks.append((t, B.make_io(t)))
+    return chunks
+
+
+def run_stream_bench(args, torch, W, B):
+    w = W.WORKLOADS[2]
+    log("bench: generating and uploading %d chunks of %s" % (w.chunks, w.name))
+    chunks = build_stream_inputs(w, torch, W, B)
+    d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
+                    chunk_start=0, window=w.window, cache_frames=w.cache_frames,
+                    query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16)
+    s = B.Stream(d)
+    stream = torch.cuda.current_stream()
+    n = w.chunks
+
+    # per-chunk layout stats (layouts cached inside the stream object)
+    flops = []
+    for ch in range(n):
+        s.seek(ch * w.C, max(0, ch * w.C - w.cache_frames))
+        flops.append(B.fa_layout_stats(s.layout())["useful_flops"])
+    s.seek(0, 0)
+
+    def step(k, ev=None):
+        ch = k % n
+        if ch == 0:
+            s.seek(0, 0)
+        t, io = chunks[ch]
+        L = s.layout()
+        if ev is not None:
+            ev[0].record(stream)
+        B.fa_attn_fwd(L, io, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        s.advance(io, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        return ch
+
+    log("bench: warmup %d steps" % args.warmup)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    log("bench: timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    chs = []
+    for k in range(args.steps):
+        chs.append(step(args.warmup + k, evs[k]))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    app_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    useful = sum(flops[c] for c in chs)
+    steady = [a for a, c in zip(attn_ms, chs) if c >= 4]
+    steady_flops = flops[n - 1]
+    bytes_chunk = B.fa_layout_stats(s.layout())["bytes"]
+    return {
+        "w": w, "total_ms": total_ms, "wall_s": wall, "useful": useful, "attn_ms": attn_ms,
+        "append_ms": app_ms, "chunks": chs, "flops": flops, "steady": steady,
+        "steady_flops": steady_flops, "bytes_steady": bytes_chunk,
+    }
+
+
+def time_single_call(wid, torch, W, B, reps=10):
+    """One-shot workloads (bidirectional 21x1560, 3600-token chunk): attention call only."""
+    w = W.WORKLOADS[wid]
+    dev = lambda x: torch.from_numpy(x).unsqueeze(0).to("cuda").to(torch.bfloat16).contiguous()
+    if wid == 1:
+        x = W.chunk_tensors(w, 0, with_queries_src_ref=True)
+        r = W.ref_tensors(w, with_queries=True)
+        t = {n: dev(v) for n, v in {**x, **r}.items()}
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
+                        query_rows=7, dtype=B.FA_BF16)
+        rows = {"tgt": w.C * w.T, "src": w.C * w.T, "ref": sum(w.ref_tokens)}
+        L = B.fa_layout_build(d)
+    else:
+        cs = w.first_cs
+        x = W.chunk_tensors(w, cs // w.C)
+        r = W.ref_tensors(w)
+        t = {n: dev(v) for n, v in {**x, **r}.items()}
+        for n in ("k_ring", "v_ring"):
+            t[n] = torch.randn((1, w.cache_frames * w.T, w.H, w.D), device="cuda").to(torch.bfloat16)
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.t0_for(cs),
+                        chunk_start=cs, window=w.window, cache_frames=w.cache_frames,
+                        query_rows=1, dtype=B.FA_BF16)
+        rows = {"tgt": w.C * w.T}
+        L = B.fa_layout_build(d, cs - w.window)
+    for nm, n in rows.items():
+        t["o_" + nm] = torch.empty((1, n, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        t["lse_" + nm] = torch.empty((1, w.H, n), dtype=torch.float32, device="cuda")
+    io = B.make_io(t)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.fa_attn_fwd(L, io, stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        B.fa_attn_fwd(L, io, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    fl = B.fa_layout_stats(L)["useful_flops"]
+    med = statistics.median(ms)
+    return {"workload": w.name, "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+            "useful_tflops": round(fl / med / 1e9, 2),
+            "mfma_frac": round(fl / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def cpu_baseline(W, budget_s):
+    """The oracle, as it stands, on a bounded sample of the steady chunk (chunk 19)."""
+    import numpy as np
+    from oracle import oracle as O
+    w = W.WORKLOADS[2]
+    H = 1
+    cs = (w.chunks - 1) * w.C
+    lo = max(0, cs - w.window)
+    ks, vs = [], []
+    for ch in range(lo // w.C, cs // w.C + 1):
+        x = W.chunk_tensors(w, ch, H=H)
+        ks.append(x["k_tgt"]); vs.append(x["v_tgt"])
+    x = W.chunk_tensors(w, cs // w.C, H=H)
+    r = W.ref_tensors(w, H=H)
+    p = O.Problem(T=w.T, C=w.C, H=H, D=w.D, cs=cs, window=w.window, hist_first=lo,
+                  ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, q_tgt=x["q_tgt"],
+                  k_hist=np.concatenate(ks), v_hist=np.concatenate(vs), k_src=x["k_src"],
+                  v_src=x["v_src"], k_ref=r["k_ref"], v_ref=r["v_ref"],
+                  q_src=np.zeros((0, H, w.D), np.float32), q_ref=np.zeros((0, H, w.D), np.float32))
+    keys = O.count(p, O.FAO_TGT, 0)
+    rows_total = w.C * w.T
+    n = 64
+    done_rows, spent = 0, 0.0
+    g = np.random.default_rng(0)
+    while spent < budget_s and done_rows < rows_total:
+        rows = g.integers(0, rows_total, size=n)
+        t0 = time.perf_counter()
+        O.attn_rows(p, [O.FAO_TGT] * n, [0] * n, rows.tolist())
+        spent += time.perf_counter() - t0
+        done_rows += n
+        n = min(4096, n * 2)
+    fl = done_rows * keys * 4 * w.D
+    return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": O.threads(),
+            "kind": "oracle",
+            "sample": "%d random target rows of head 0 of the steady chunk (chunk 19, %d visible "
+                      "keys each) of the 1560-token 40-head stream, %.1f s" % (done_rows, keys, spent)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other bf16 workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the attention "
+              "shards by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fa_workloads as W
+    from frame_aligned_attention_amd import binding as B
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    res = run_stream_bench(args, torch, W, B)
+    w = res["w"]
+    value = res["useful"] / res["total_ms"] / 1e9  # TFLOP/s
+    ms_step = res["total_ms"] / args.steps
+    attn_mean = statistics.mean(res["attn_ms"])
+    useful_per_launch = res["useful"] / args.steps
+    achieved = useful_per_launch / attn_mean / 1e9
+    traffic = traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: 20-chunk stream, 3 frames x 1560 tokens per chunk, window 12 "
+                               "frames, ring 12 frames, 1560 reference tokens, 40 heads, head_dim "
+                               "128, batch 1; step = attention + ring append of one chunk" % w.name,
+                   "tokens_per_frame": w.T, "chunk_frames": w.C, "heads": w.H,
+                   "head_dim": w.D, "window": w.window, "ring_frames": w.cache_frames,
+                   "ref_tokens": sum(w.ref_tokens)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "attn_ms_mean": round(attn_mean, 4),
+        "attn_ms_steady_median": round(statistics.median(res["steady"]), 4) if res["steady"] else None,
+        "steady_chunk_tflops": round(res["steady_flops"] / statistics.median(res["steady"]) / 1e9, 2)
+        if res["steady"] else None,
+        "append_ms_mean": round(statistics.mean(res["append_ms"]), 4),
+        "steady_chunk_hbm_gbs": round(res["bytes_steady"] / statistics.median(res["steady"]) / 1e6, 1)
+        if res["steady"] else None,
+        "wall_s": round(res["wall_s"], 3),
+    }
+    if not args.no_extra:
+        log("bench: other bf16 workloads")
+        out["other_workloads"] = [time_single_call(1, torch, W, B), time_single_call(3, torch, W, B)]
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,266 @@
+"""ctypes binding of libfa.so (include/fa.h).
+
+Argument marshalling only: torch tensors (device memory) and the current torch
+stream are turned into the C structures of fa.h, and every call goes to the
+library.  There is no fallback: if libfa.so is missing, importing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_CAPACITY, FA_ERR_HIP, FA_ERR_NOMEM = \
+    0, -1, -2, -3, -4, -5
+FA_F32, FA_BF16, FA_LOWBIT = 0, 1, 2
+FA_Q_TARGET, FA_Q_SOURCE, FA_Q_REF = 1, 2, 4
+FA_WINDOW_ALL = -1
+FA_MAX_REF = 8
+FA_SEG_RING, FA_SEG_TGT, FA_SEG_SRC, FA_SEG_REF = 0, 1, 2, 3
+FA_MASK_NONE, FA_MASK_SAME_FRAME, FA_MASK_GATE = 0, 1, 2
+FA_QUANT_MEAN_GIVEN = 1
+
+
+class fa_layout_desc(C.Structure):
+    _fields_ = [("frames", C.c_int32), ("tokens_per_frame", C.c_int32), ("n_ref", C.c_int32),
+                ("ref_tokens", C.c_int32 * FA_MAX_REF), ("ref_t0", C.c_int32 * FA_MAX_REF),
+                ("chunk_start", C.c_int32), ("window", C.c_int32), ("cache_frames", C.c_int32),
+                ("query_rows", C.c_int32), ("batch", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("dtype", C.c_int32), ("scale", C.c_float)]
+
+
+class fa_tensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("stride_b", C.c_int64), ("stride_n", C.c_int64),
+                ("stride_h", C.c_int64), ("scale", C.c_void_p)]
+
+
+_IO_TENSORS = ["q_tgt", "q_src", "q_ref", "k_ring", "v_ring", "k_tgt", "v_tgt", "k_src", "v_src",
+               "k_ref", "v_ref", "o_tgt", "o_src", "o_ref"]
+_IO_PTRS = ["lse_tgt", "lse_src", "lse_ref", "k_mean", "v_absmax"]
+
+
+class fa_io(C.Structure):
+    _fields_ = [(n, fa_tensor) for n in _IO_TENSORS] + [(n, C.c_void_p) for n in _IO_PTRS]
+
+
+class fa_tile_info(C.Structure):
+    _fields_ = [("q_kind", C.c_int32), ("row0", C.c_int32), ("rows", C.c_int32),
+                ("n_ranges", C.c_int32)]
+
+
+class fa_range_info(C.Structure):
+    _fields_ = [("seg", C.c_int32), ("begin", C.c_int32), ("end", C.c_int32), ("mask", C.c_int32),
+                ("param", C.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfa.so is not built (%s); run __graft_entry__.build() or "
+                          "python frame_aligned_attention_amd/build.py" % LIB_PATH)
+    lib = C.CDLL(LIB_PATH)
+    P = C.c_void_p
+    sig = {
+        "fa_status_str": ([C.c_int], C.c_char_p),
+        "fa_last_error": ([], C.c_char_p),
+        "fa_layout_build": ([C.POINTER(fa_layout_desc), C.c_int32, C.POINTER(P)], C.c_int),
+        "fa_layout_stats": ([P] + [C.POINTER(C.c_double)] * 4, C.c_int),
+        "fa_layout_tiles": ([P] + [C.POINTER(C.c_int32)] * 3, C.c_int),
+        "fa_layout_tile": ([P, C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
+                            C.c_int32], C.c_int),
+        "fa_layout_destroy": ([P], C.c_int),
+        "fa_attn_fwd": ([P, C.POINTER(fa_io), P], C.c_int),
+        "fa_quantize_lowbit": ([P, C.POINTER(fa_io), C.POINTER(fa_io), C.c_int32, P], C.c_int),
+        "fa_ring_append": ([C.POINTER(fa_layout_desc)] + [C.POINTER(fa_tensor)] * 4 +
+                           [C.c_int32, C.c_int32, P], C.c_int),
+        "fa_stream_create": ([C.POINTER(fa_layout_desc), C.POINTER(P)], C.c_int),
+        "fa_stream_chunk": ([P, C.POINTER(fa_io), P], C.c_int),
+        "fa_stream_advance": ([P, C.POINTER(fa_io), P], C.c_int),
+        "fa_stream_layout": ([P, C.POINTER(P)], C.c_int),
+        "fa_stream_state": ([P, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
+        "fa_stream_seek": ([P, C.c_int32, C.c_int32], C.c_int),
+        "fa_stream_set_refs": ([P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
+        "fa_stream_destroy": ([P], C.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.fa_last_error().decode()
+        super().__init__("%s: %s (%s)" % (where, lib.fa_status_str(status).decode(), msg))
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def make_desc(frames: int, tokens_per_frame: int, heads: int, head_dim: int, *, batch: int = 1,
+              ref_tokens: Sequence[int] = (), ref_t0: Sequence[int] = (), chunk_start: int = 0,
+              window: int = 0, cache_frames: int = 0, query_rows: int = FA_Q_TARGET,
+              dtype: int = FA_BF16, scale: float = 0.0) -> fa_layout_desc:
+    d = fa_layout_desc()
+    d.frames, d.tokens_per_frame = frames, tokens_per_frame
+    d.n_ref = len(ref_tokens)
+    for i, (n, t0) in enumerate(zip(ref_tokens, ref_t0)):
+        d.ref_tokens[i], d.ref_t0[i] = int(n), int(t0)
+    d.chunk_start, d.window, d.cache_frames = chunk_start, window, cache_frames
+    d.query_rows, d.batch, d.heads, d.head_dim = query_rows, batch, heads, head_dim
+    d.dtype, d.scale = dtype, scale
+    return d
+
+
+def tensor(t, scale=None) -> fa_tensor:
+    """fa_tensor of a [B, N, H, D] or [N, H, D] torch tensor (head_dim contiguous)."""
+    if t is None:
+        return fa_tensor()
+    if t.dim() == 3:
+        sb, sn, sh = 0, t.stride(0), t.stride(1)
+        dstride = t.stride(2)
+    elif t.dim() == 4:
+        sb, sn, sh = t.stride(0), t.stride(1), t.stride(2)
+        dstride = t.stride(3)
+    else:
+        raise ValueError("expected a [B,N,H,D] or [N,H,D] tensor")
+    if dstride != 1 and t.shape[-1] > 1:
+        raise ValueError("head_dim axis must be contiguous")
+    return fa_tensor(t.data_ptr(), sb, sn, sh, scale.data_ptr() if scale is not None else None)
+
+
+def make_io(tensors: Dict[str, object], scales: Optional[Dict[str, object]] = None) -> fa_io:
+    io = fa_io()
+    scales = scales or {}
+    for n in _IO_TENSORS:
+        if tensors.get(n) is not None:
+            setattr(io, n, tensor(tensors[n], scales.get(n)))
+    for n in _IO_PTRS:
+        if tensors.get(n) is not None:
+            setattr(io, n, tensors[n].data_ptr())
+    return io
+
+
+class Layout:
+    """Owns an fa_layout*."""
+
+    def __init__(self, handle, owned=True):
+        self.handle = handle
+        self.owned = owned
+
+    def __del__(self):
+        if getattr(self, "owned", False) and self.handle:
+            lib.fa_layout_destroy(self.handle)
+            self.handle = None
+
+
+def fa_layout_build(desc: fa_layout_desc, ring_first_frame: int = -1) -> Layout:
+    h = C.c_void_p()
+    _check(lib.fa_layout_build(C.byref(desc), ring_first_frame, C.byref(h)), "fa_layout_build")
+    return Layout(h)
+
+
+def fa_layout_stats(L: Layout) -> dict:
+    v = [C.c_double() for _ in range(4)]
+    _check(lib.fa_layout_stats(L.handle, *[C.byref(x) for x in v]), "fa_layout_stats")
+    return {"useful_pairs": v[0].value, "useful_flops": v[1].value, "visited_pairs": v[2].value,
+            "bytes": v[3].value}
+
+
+def fa_layout_tiles(L: Layout):
+    n, bm, bn = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib.fa_layout_tiles(L.handle, C.byref(n), C.byref(bm), C.byref(bn)), "fa_layout_tiles")
+    return n.value, bm.value, bn.value
+
+
+def fa_layout_tile(L: Layout, i: int):
+    t = fa_tile_info()
+    rr = (fa_range_info * 64)()
+    _check(lib.fa_layout_tile(L.handle, i, C.byref(t), rr, 64), "fa_layout_tile")
+    ranges = [(r.seg, r.begin, r.end, r.mask, r.param) for r in rr[:t.n_ranges]]
+    return (t.q_kind, t.row0, t.rows), ranges
+
+
+def fa_layout_destroy(L: Layout):
+    if L.handle:
+        _check(lib.fa_layout_destroy(L.handle), "fa_layout_destroy")
+        L.handle = None
+
+
+def fa_attn_fwd(L: Layout, io: fa_io, stream=None):
+    _check(lib.fa_attn_fwd(L.handle, C.byref(io), _stream_handle(stream)), "fa_attn_fwd")
+
+
+def fa_quantize_lowbit(L: Layout, io_in: fa_io, io_out: fa_io, flags: int = 0, stream=None):
+    _check(lib.fa_quantize_lowbit(L.handle, C.byref(io_in), C.byref(io_out), flags,
+                                  _stream_handle(stream)), "fa_quantize_lowbit")
+
+
+def fa_ring_append(desc: fa_layout_desc, k_ring, v_ring, k_chunk, v_chunk, first_frame: int,
+                   frames: int, stream=None):
+    ts = [tensor(x) for x in (k_ring, v_ring, k_chunk, v_chunk)]
+    _check(lib.fa_ring_append(C.byref(desc), *[C.byref(t) for t in ts], first_frame, frames,
+                              _stream_handle(stream)), "fa_ring_append")
+
+
+class Stream:
+    """Owns an fa_stream* (the streaming driver)."""
+
+    def __init__(self, desc: fa_layout_desc):
+        h = C.c_void_p()
+        _check(lib.fa_stream_create(C.byref(desc), C.byref(h)), "fa_stream_create")
+        self.handle = h
+        self.desc = desc
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.fa_stream_destroy(self.handle)
+            self.handle = None
+
+    def chunk(self, io: fa_io, stream=None):
+        _check(lib.fa_stream_chunk(self.handle, C.byref(io), _stream_handle(stream)),
+               "fa_stream_chunk")
+
+    def advance(self, io: fa_io, stream=None):
+        _check(lib.fa_stream_advance(self.handle, C.byref(io), _stream_handle(stream)),
+               "fa_stream_advance")
+
+    def layout(self) -> Layout:
+        h = C.c_void_p()
+        _check(lib.fa_stream_layout(self.handle, C.byref(h)), "fa_stream_layout")
+        return Layout(h, owned=False)
+
+    def state(self):
+        a, b = C.c_int32(), C.c_int32()
+        _check(lib.fa_stream_state(self.handle, C.byref(a), C.byref(b)), "fa_stream_state")
+        return a.value, b.value
+
+    def seek(self, next_frame: int, ring_first_frame: int):
+        _check(lib.fa_stream_seek(self.handle, next_frame, ring_first_frame), "fa_stream_seek")
+
+    def set_refs(self, ref_tokens: Sequence[int], ref_t0: Sequence[int]):
+        n = len(ref_tokens)
+        a = (C.c_int32 * max(n, 1))(*ref_tokens)
+        b = (C.c_int32 * max(n, 1))(*ref_t0)
+        _check(lib.fa_stream_set_refs(self.handle, n, a, b), "fa_stream_set_refs")
+
+
+def fa_stream_create(desc: fa_layout_desc) -> Stream:
+    return Stream(desc)

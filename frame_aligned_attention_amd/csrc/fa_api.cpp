@@ -1,0 +1,348 @@
+// fa_api.cpp -- the C ABI: errors, I/O validation, kernel dispatch, ring
+// append and the streaming driver.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "fa_layout_impl.h"
+
+namespace fa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+fa_status fail(fa_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+static int elem_q(int dtype) { return dtype == FA_F32 ? 4 : dtype == FA_BF16 ? 2 : 1; }
+static int elem_o(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+static fa_status check_tensor(const fa_tensor &t, int esize, int batch, const char *name,
+                              bool need_scale) {
+  if (!t.data) return fail(FA_ERR_INVALID, std::string(name) + ": data is NULL");
+  const uintptr_t p = (uintptr_t)t.data;
+  if (p % 16) return fail(FA_ERR_INVALID, std::string(name) + ": base pointer not 16-byte aligned");
+  if ((t.stride_n * esize) % 16 || (t.stride_h * esize) % 16 ||
+      (batch > 1 && (t.stride_b * esize) % 16))
+    return fail(FA_ERR_INVALID, std::string(name) + ": strides keep rows 16-byte aligned only if "
+                                                    "stride*element_size is a multiple of 16");
+  if (t.stride_n < 0 || t.stride_h < 0 || t.stride_b < 0)
+    return fail(FA_ERR_INVALID, std::string(name) + ": negative stride");
+  if (need_scale && !t.scale)
+    return fail(FA_ERR_INVALID, std::string(name) + ": low-bit scale array is NULL");
+  return FA_OK;
+}
+
+static Seg seg_of(const fa_tensor &t, int ntok) {
+  Seg s{};
+  s.p = t.data;
+  s.sb = t.stride_b;
+  s.sn = t.stride_n;
+  s.sh = t.stride_h;
+  s.scale = t.scale;
+  s.nblk = (ntok + kQuantBlock - 1) / kQuantBlock;
+  return s;
+}
+
+static const char *kQName[3] = {"q_tgt", "q_src", "q_ref"};
+static const char *kOName[3] = {"o_tgt", "o_src", "o_ref"};
+static const char *kKName[4] = {"k_ring", "k_tgt", "k_src", "k_ref"};
+static const char *kVName[4] = {"v_ring", "v_tgt", "v_src", "v_ref"};
+
+static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t stream) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (!io) return fail(FA_ERR_INVALID, "io is NULL");
+  const fa_layout_desc &d = L->d;
+  const bool low = d.dtype == FA_LOWBIT;
+  const int eq = elem_q(d.dtype), eo = elem_o(d.dtype);
+  const fa_tensor *qs[3] = {&io->q_tgt, &io->q_src, &io->q_ref};
+  const fa_tensor *os[3] = {&io->o_tgt, &io->o_src, &io->o_ref};
+  const fa_tensor *ks[4] = {&io->k_ring, &io->k_tgt, &io->k_src, &io->k_ref};
+  const fa_tensor *vs[4] = {&io->v_ring, &io->v_tgt, &io->v_src, &io->v_ref};
+  float *lses[3] = {io->lse_tgt, io->lse_src, io->lse_ref};
+  const int T = d.tokens_per_frame;
+  const int seg_tok[4] = {d.cache_frames * T, d.frames * T, d.frames * T, L->ref_total};
+  bool used[4] = {false, false, false, false};
+  for (const DevRange &r : L->ranges) used[r.seg] = true;
+  AttnArgs a{};
+  for (int k = 0; k < 3; ++k) {
+    if (!L->q_rows[k]) continue;
+    fa_status st = check_tensor(*qs[k], eq, d.batch, kQName[k], low);
+    if (st != FA_OK) return st;
+    st = check_tensor(*os[k], eo, d.batch, kOName[k], false);
+    if (st != FA_OK) return st;
+    if (lses[k] && ((uintptr_t)lses[k]) % 4) return fail(FA_ERR_INVALID, "lse not 4-byte aligned");
+    a.q[k] = seg_of(*qs[k], L->q_rows[k]);
+    a.o[k] = seg_of(*os[k], L->q_rows[k]);
+    a.lse[k] = lses[k];
+    a.q_rows[k] = L->q_rows[k];
+  }
+  for (int s = 0; s < 4; ++s) {
+    if (!used[s]) continue;
+    fa_status st = check_tensor(*ks[s], eq, d.batch, kKName[s], low);
+    if (st != FA_OK) return st;
+    st = check_tensor(*vs[s], eq, d.batch, kVName[s], low);
+    if (st != FA_OK) return st;
+    a.k[s] = seg_of(*ks[s], seg_tok[s]);
+    a.v[s] = seg_of(*vs[s], seg_tok[s]);
+  }
+  if (low && !io->v_absmax) return fail(FA_ERR_INVALID, "v_absmax is NULL");
+  a.v_absmax = io->v_absmax;
+  a.T = T;
+  a.H = d.heads;
+  a.scale = d.scale;
+  a.c = d.scale * 1.4426950408889634f;
+  if (L->work.empty()) return FA_OK;
+  DeviceMap m;
+  fa_status st = device_map(L, &m);
+  if (st != FA_OK) return st;
+  a.tiles = m.tiles;
+  a.ranges = m.ranges;
+  a.work = m.work;
+  const int grid = (int)L->work.size();
+  hipError_t e;
+  if (d.dtype == FA_F32)
+    e = launch_attn_f32(a, d.head_dim, grid, stream);
+  else if (d.dtype == FA_BF16)
+    e = launch_attn_bf16(a, d.head_dim, grid, stream);
+  else
+    e = launch_attn_lowbit(a, d.head_dim, grid, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+static fa_status ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
+                             const fa_tensor *v_ring, const fa_tensor *k_chunk,
+                             const fa_tensor *v_chunk, int32_t first_frame, int32_t frames,
+                             hipStream_t stream) {
+  if (!d || !k_ring || !v_ring || !k_chunk || !v_chunk)
+    return fail(FA_ERR_INVALID, "NULL argument");
+  if (d->cache_frames < 1) return fail(FA_ERR_INVALID, "cache_frames must be >= 1 to append");
+  if (d->tokens_per_frame < 1 || d->heads < 1 || d->batch < 1)
+    return fail(FA_ERR_INVALID, "bad geometry");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim");
+  if (frames < 0 || frames > d->cache_frames)
+    return fail(FA_ERR_INVALID, "frames must be in [0, cache_frames]");
+  if (first_frame < 0) return fail(FA_ERR_INVALID, "first_frame must be >= 0");
+  if (frames == 0) return FA_OK;
+  const int es = d->dtype == FA_F32 ? 4 : 2;
+  const fa_tensor *t[4] = {k_ring, v_ring, k_chunk, v_chunk};
+  const char *nm[4] = {"k_ring", "v_ring", "k_chunk", "v_chunk"};
+  for (int i = 0; i < 4; ++i) {
+    fa_status st = check_tensor(*t[i], es, d->batch, nm[i], false);
+    if (st != FA_OK) return st;
+  }
+  RingArgs a{};
+  for (int i = 0; i < 2; ++i) {
+    const fa_tensor &s = i ? *v_chunk : *k_chunk;
+    const fa_tensor &r = i ? *v_ring : *k_ring;
+    a.src[i] = s.data;
+    a.dst[i] = r.data;
+    a.ssb[i] = s.stride_b * es; a.ssn[i] = s.stride_n * es; a.ssh[i] = s.stride_h * es;
+    a.dsb[i] = r.stride_b * es; a.dsn[i] = r.stride_n * es; a.dsh[i] = r.stride_h * es;
+  }
+  a.T = d->tokens_per_frame;
+  a.H = d->heads;
+  a.frames = frames;
+  a.first_frame = first_frame;
+  a.cache_frames = d->cache_frames;
+  a.chunks16 = d->head_dim * es / 16;
+  a.batch = d->batch;
+  hipError_t e = launch_ring_append(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("ring append: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" const char *fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_CAPACITY: return "FA_ERR_CAPACITY";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_NOMEM: return "FA_ERR_NOMEM";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+extern "C" const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream) {
+  return attn_fwd(L, io, (hipStream_t)stream);
+}
+
+extern "C" fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
+                                    const fa_tensor *v_ring, const fa_tensor *k_chunk,
+                                    const fa_tensor *v_chunk, int32_t first_frame, int32_t frames,
+                                    fa_hip_stream stream) {
+  return ring_append(d, k_ring, v_ring, k_chunk, v_chunk, first_frame, frames,
+                     (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- streaming driver
+
+struct fa_stream {
+  fa_layout_desc d;
+  int32_t next_frame = 0;
+  int32_t ring_first = 0;
+  std::vector<fa_layout *> cache;  // distinct block maps seen so far
+  fa_layout *current = nullptr;    // layout of the next chunk
+};
+
+namespace fa {
+
+static bool same_map(const fa_layout *a, const fa_layout *b) {
+  if (a->tiles.size() != b->tiles.size() || a->ranges.size() != b->ranges.size() ||
+      a->work.size() != b->work.size())
+    return false;
+  // descriptors may differ only in chunk_start / ref_t0, both folded into the ranges
+  fa_layout_desc x = a->d, y = b->d;
+  x.chunk_start = y.chunk_start = 0;
+  for (int r = 0; r < FA_MAX_REF; ++r) x.ref_t0[r] = y.ref_t0[r] = 0;
+  if (std::memcmp(&x, &y, sizeof(fa_layout_desc)) != 0) return false;
+  return std::memcmp(a->tiles.data(), b->tiles.data(), a->tiles.size() * sizeof(DevTile)) == 0 &&
+         std::memcmp(a->ranges.data(), b->ranges.data(), a->ranges.size() * sizeof(DevRange)) == 0 &&
+         std::memcmp(a->work.data(), b->work.data(), a->work.size() * sizeof(DevWork)) == 0;
+}
+
+// Layout of the chunk at s->next_frame, shared with an earlier chunk when the block map is the
+// same (steady state repeats with the ring's period).  Stats of shared layouts are identical
+// too, since they are functions of the block map and geometry.
+static fa_status stream_layout(fa_stream *s, fa_layout **out) {
+  if (s->current) {
+    *out = s->current;
+    return FA_OK;
+  }
+  fa_layout_desc d = s->d;
+  d.chunk_start = s->next_frame;
+  fa_layout *L = nullptr;
+  fa_status st = fa_layout_build(&d, s->ring_first, &L);
+  if (st != FA_OK) return st;
+  for (fa_layout *c : s->cache)
+    if (same_map(c, L)) {
+      fa_layout_destroy(L);
+      s->current = c;
+      *out = c;
+      return FA_OK;
+    }
+  if (s->cache.size() >= 64) {
+    fa_layout_destroy(s->cache.front());
+    s->cache.erase(s->cache.begin());
+  }
+  s->cache.push_back(L);
+  s->current = L;
+  *out = L;
+  return FA_OK;
+}
+
+static void stream_reset_cache(fa_stream *s) {
+  for (fa_layout *c : s->cache) fa_layout_destroy(c);
+  s->cache.clear();
+  s->current = nullptr;
+}
+
+}  // namespace fa
+
+extern "C" fa_status fa_stream_create(const fa_layout_desc *d, fa_stream **out) {
+  if (!out) return fail(FA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!d) return fail(FA_ERR_INVALID, "descriptor is NULL");
+  if (d->cache_frames < 1) return fail(FA_ERR_INVALID, "a stream needs cache_frames >= 1");
+  fa_layout *probe = nullptr;  // validates the geometry at the first chunk position
+  fa_status st = fa_layout_build(d, d->chunk_start, &probe);
+  if (st == FA_ERR_CAPACITY) st = fa_layout_build(d, -1, &probe);
+  if (st != FA_OK) return st;
+  fa_layout_destroy(probe);
+  fa_stream *s = new (std::nothrow) fa_stream();
+  if (!s) return fail(FA_ERR_NOMEM, "host allocation failed");
+  s->d = *d;
+  s->next_frame = d->chunk_start;
+  s->ring_first = d->chunk_start;
+  *out = s;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_stream_layout(fa_stream *s, const fa_layout **out) {
+  if (!s || !out) return fail(FA_ERR_INVALID, "NULL argument");
+  fa_layout *L = nullptr;
+  fa_status st = stream_layout(s, &L);
+  *out = L;
+  return st;
+}
+
+extern "C" fa_status fa_stream_advance(fa_stream *s, const fa_io *io, fa_hip_stream stream) {
+  if (!s || !io) return fail(FA_ERR_INVALID, "NULL argument");
+  fa_status st = ring_append(&s->d, &io->k_ring, &io->v_ring, &io->k_tgt, &io->v_tgt,
+                             s->next_frame, s->d.frames, (hipStream_t)stream);
+  if (st != FA_OK) return st;
+  s->next_frame += s->d.frames;
+  s->ring_first = std::max(s->ring_first, s->next_frame - s->d.cache_frames);
+  s->current = nullptr;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_stream_chunk(fa_stream *s, const fa_io *io, fa_hip_stream stream) {
+  if (!s || !io) return fail(FA_ERR_INVALID, "NULL argument");
+  if (s->d.dtype == FA_LOWBIT)
+    return fail(FA_ERR_UNSUPPORTED,
+                "low-bit streams: fa_stream_layout, fa_quantize_lowbit, fa_attn_fwd, then "
+                "fa_stream_advance");
+  fa_layout *L = nullptr;
+  fa_status st = stream_layout(s, &L);
+  if (st != FA_OK) return st;
+  st = attn_fwd(L, io, (hipStream_t)stream);
+  if (st != FA_OK) return st;
+  return fa_stream_advance(s, io, stream);
+}
+
+extern "C" fa_status fa_stream_state(const fa_stream *s, int32_t *next_frame,
+                                     int32_t *ring_first_frame) {
+  if (!s) return fail(FA_ERR_INVALID, "stream is NULL");
+  if (next_frame) *next_frame = s->next_frame;
+  if (ring_first_frame) *ring_first_frame = s->ring_first;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_stream_seek(fa_stream *s, int32_t next_frame, int32_t ring_first_frame) {
+  if (!s) return fail(FA_ERR_INVALID, "stream is NULL");
+  if (next_frame < 0 || ring_first_frame < 0 || ring_first_frame > next_frame ||
+      next_frame - ring_first_frame > s->d.cache_frames)
+    return fail(FA_ERR_INVALID, "inconsistent stream state");
+  s->next_frame = next_frame;
+  s->ring_first = ring_first_frame;
+  s->current = nullptr;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_stream_set_refs(fa_stream *s, int32_t n_ref, const int32_t *ref_tokens,
+                                        const int32_t *ref_t0) {
+  if (!s) return fail(FA_ERR_INVALID, "stream is NULL");
+  if (n_ref < 0 || n_ref > FA_MAX_REF || (n_ref > 0 && (!ref_tokens || !ref_t0)))
+    return fail(FA_ERR_INVALID, "bad reference set");
+  for (int r = 0; r < n_ref; ++r)
+    if (ref_tokens[r] < 0) return fail(FA_ERR_INVALID, "ref_tokens must be >= 0");
+  s->d.n_ref = n_ref;
+  for (int r = 0; r < FA_MAX_REF; ++r) {
+    s->d.ref_tokens[r] = r < n_ref ? ref_tokens[r] : 0;
+    s->d.ref_t0[r] = r < n_ref ? ref_t0[r] : 0;
+  }
+  stream_reset_cache(s);
+  return FA_OK;
+}
+
+extern "C" fa_status fa_stream_destroy(fa_stream *s) {
+  if (!s) return FA_OK;
+  stream_reset_cache(s);
+  delete s;
+  return FA_OK;
+}

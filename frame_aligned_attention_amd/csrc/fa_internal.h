@@ -1,0 +1,114 @@
+// fa_internal.h -- structures shared by the host side of libfa.so and its
+// gfx950 kernels: the device form of a layout's block map and the kernel
+// argument blocks.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+// Tile sizes of the kernels.  The block map is built for the kernel that
+// will consume it: BM query rows per tile, key tiles of BN keys.
+constexpr int kBf16BlockM = 128;   // 4 waves x 32 query rows
+constexpr int kBf16BlockN = 64;
+constexpr int kF32BlockM = 64;     // one wave, one row per lane
+constexpr int kF32BlockN = 64;
+constexpr int kLowbitBlockM = 128;
+constexpr int kLowbitBlockN = 64;
+constexpr int kQuantBlock = 128;   // tokens per quantisation block
+
+// One key range of a tile.  seg: FA_SEG_*; mask: FA_MASK_*.
+struct DevRange {
+  int32_t seg;
+  int32_t mask;
+  int32_t begin;
+  int32_t end;
+  int32_t param;
+  int32_t pad[3];
+};
+
+// One tile of query rows.  Ranges [r_begin, r_begin + r_count) of the map.
+struct DevTile {
+  int32_t q_kind;
+  int32_t row0;
+  int32_t rows;
+  int32_t r_begin;
+  int32_t r_count;
+  int32_t pad[3];
+};
+
+// Grid slot -> (tile, batch*heads + head); tile < 0 marks an idle slot.
+struct DevWork {
+  int32_t tile;
+  int32_t bh;
+};
+
+// A device tensor: base pointer and element strides (head_dim contiguous).
+struct Seg {
+  const void *p;
+  int64_t sb, sn, sh;
+  const float *scale;  // low-bit per-block scales [b][h][nblk]
+  int32_t nblk;
+  int32_t pad;
+};
+
+struct AttnArgs {
+  Seg k[4];          // by FA_SEG_*
+  Seg v[4];
+  Seg q[3];          // by query kind
+  Seg o[3];
+  float *lse[3];
+  int32_t q_rows[3]; // rows per query kind (LSE row stride)
+  int32_t T;
+  int32_t H;
+  float scale;       // softmax scale
+  float c;           // scale * log2(e)
+  const DevTile *tiles;
+  const DevRange *ranges;
+  const DevWork *work;
+  const float *v_absmax;  // low-bit: [b][h]
+};
+
+struct RingArgs {
+  const void *src[2];
+  void *dst[2];
+  int64_t ssb[2], ssn[2], ssh[2];
+  int64_t dsb[2], dsn[2], dsh[2];
+  int32_t T, H, frames, first_frame, cache_frames, chunks16;  // 16-byte chunks per (token, head)
+  int32_t batch;
+};
+
+// Launchers (defined in the .hip files); return hipError_t of the launch.
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attn_lowbit(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
+
+struct QuantSeg {
+  const void *in;         // bf16
+  int64_t isb, isn, ish;
+  void *out;              // int8 or e4m3 codes
+  int64_t osb, osn, osh;
+  float *scale;           // [b][h][nblk]
+  int32_t n;              // tokens
+  int32_t kind;           // 0: Q (int8), 1: K (int8, mean-subtracted), 2: V (e4m3)
+  // ring segments: only tokens of frames in view are quantised
+  int32_t ring_lo_tok, ring_hi_tok;   // token range [lo, hi) in view; or whole segment
+  int32_t ring_lo2_tok, ring_hi2_tok; // second run (wrap); empty if lo2 >= hi2
+};
+
+struct QuantArgs {
+  QuantSeg seg[11];
+  int32_t nseg;
+  int32_t H, D, batch;
+  float *k_mean;          // [b][h][D]
+  float *v_absmax;        // [b][h]
+  int32_t mean_given;
+};
+
+hipError_t launch_quant_lowbit(const QuantArgs &a, hipStream_t s);
+
+}  // namespace fa

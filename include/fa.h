@@ -1,0 +1,248 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) frame-aligned attention library (libfa.so).
+ *
+ * The operation.  Frame-aligned attention as the "Vidu S2" pages describe it
+ * (tech report text, paragraphs on frame-aligned attention and on causal
+ * streaming editing; structured summary sections 3.3, 4.3 and 5.2; news
+ * clipping point 7).  Three token streams meet in one softmax attention:
+ *   target  -- the frames being generated; F frames of T tokens,
+ *   source  -- the input video, one frame of T tokens per target frame,
+ *   reference images -- n_ref images of ref_tokens[r] tokens.
+ * A target row of absolute frame f sees:
+ *   - target keys of every frame of the call (bidirectional model), or, when
+ *     streaming block-wise causally, of the current chunk plus the `window`
+ *     frames before it (history held in a ring-buffer KV cache);
+ *   - source keys of frame f only;
+ *   - reference image r iff f >= ref_t0[r] (timestamp-aligned reference).
+ * Source rows (when asked for) see their own frame's source keys and the
+ * gated references; reference rows see all reference keys.  Scores are
+ * scale * q.k, the softmax is exact; outputs are O and the natural-log
+ * log-sum-exp LSE of the visible scores.
+ *
+ * Conventions.
+ *  - Every call returns fa_status; nothing throws across the ABI.
+ *    Descriptor, shape, pointer and alignment checks run on the host before
+ *    anything is enqueued; a failed check returns FA_ERR_INVALID /
+ *    FA_ERR_UNSUPPORTED / FA_ERR_CAPACITY and enqueues nothing.  A HIP
+ *    launch failure returns FA_ERR_HIP.  Faults inside kernels surface at
+ *    the caller's next synchronisation.  fa_last_error() gives a
+ *    thread-local text for the last failure.
+ *  - Device tensors are token-major [batch][tokens][heads][head_dim] with the
+ *    head_dim axis contiguous; other strides are free (fa_tensor).  Base
+ *    pointers and the b/n/h strides must keep every row 16-byte aligned.
+ *  - The caller owns every tensor.  The library owns only what it allocates
+ *    for a layout or a stream object (a small device block map) and frees it
+ *    in the matching destroy call.  fa_attn_fwd allocates nothing.
+ *  - Work is enqueued on the caller's HIP stream (with PyTorch-ROCm, the
+ *    current torch stream) and is asynchronous.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *fa_hip_stream; /* hipStream_t; NULL = the default stream */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,     /* malformed descriptor, pointer, stride or argument */
+  FA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, dtype, sizes beyond limits */
+  FA_ERR_CAPACITY = -3,    /* the ring cannot hold the history the call needs */
+  FA_ERR_HIP = -4,         /* a HIP runtime call failed */
+  FA_ERR_NOMEM = -5        /* host or device allocation failed */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,    /* fp32 in, fp32 out, fp32 arithmetic */
+  FA_BF16 = 1,   /* bf16 in, bf16 out, fp32 softmax and accumulation */
+  FA_LOWBIT = 2  /* int8 Q/K (per-128-token block scales), fp8 e4m3 V and P, fp32 softmax */
+} fa_dtype;
+
+enum { FA_Q_TARGET = 1, FA_Q_SOURCE = 2, FA_Q_REF = 4 };
+
+#define FA_WINDOW_ALL (-1)
+#define FA_MAX_REF 8
+
+/*
+ * One call's geometry.  Bidirectional model: chunk_start = 0, window = 0,
+ * cache_frames = 0, frames = F.  Streaming: frames = C (the chunk),
+ * chunk_start = absolute frame of the chunk's first frame, window = history
+ * frames kept visible before it (block-wise causal: every row of the chunk
+ * sees the same history), cache_frames = ring capacity in frames.
+ */
+typedef struct {
+  int32_t frames;           /* query frames in the call (F or C), >= 1 */
+  int32_t tokens_per_frame; /* T, target and source alike, >= 1 */
+  int32_t n_ref;            /* reference images, 0 .. FA_MAX_REF (the reference is optional) */
+  int32_t ref_tokens[FA_MAX_REF]; /* tokens of each image, stored back to back in k_ref/v_ref */
+  int32_t ref_t0[FA_MAX_REF];     /* absolute frame from which image r is visible */
+  int32_t chunk_start;      /* absolute frame index of query frame 0 */
+  int32_t window;           /* history frames visible before chunk_start; FA_WINDOW_ALL = all */
+  int32_t cache_frames;     /* ring capacity in frames; 0 = no ring (no history) */
+  int32_t query_rows;       /* FA_Q_* bits: which rows are queries */
+  int32_t batch, heads, head_dim; /* head_dim 64 or 128; query heads == key heads */
+  int32_t dtype;            /* fa_dtype */
+  float scale;              /* softmax scale; 0 = 1/sqrt(head_dim) */
+} fa_layout_desc;
+
+/* A device tensor [batch][tokens][heads][head_dim], head_dim contiguous. */
+typedef struct {
+  void *data;                           /* element [0][0][0][0]; NULL = absent */
+  int64_t stride_b, stride_n, stride_h; /* in elements */
+  float *scale;                         /* FA_LOWBIT: per-block scales [batch][heads][ceil(tokens/128)] */
+} fa_tensor;
+
+/*
+ * Every tensor of one call.  Rows: q_tgt/o_tgt frames*T, q_src/o_src
+ * frames*T, q_ref/o_ref sum(ref_tokens).  Keys: k/v_tgt are the call's own
+ * target frames (frames*T), k/v_src the same frames' source (frames*T),
+ * k/v_ref the references, k/v_ring the ring (cache_frames*T; absolute frame
+ * g lives in slot g mod cache_frames, tokens [slot*T, slot*T+T)).
+ * lse_*: [batch][heads][rows] fp32, NULL to skip.  Outputs of kinds not in
+ * query_rows may be absent.
+ */
+typedef struct {
+  fa_tensor q_tgt, q_src, q_ref;
+  fa_tensor k_ring, v_ring;
+  fa_tensor k_tgt, v_tgt, k_src, v_src, k_ref, v_ref;
+  fa_tensor o_tgt, o_src, o_ref;
+  float *lse_tgt, *lse_src, *lse_ref;
+  float *k_mean;   /* FA_LOWBIT quantiser: per-head channel mean [batch][heads][head_dim] */
+  float *v_absmax; /* FA_LOWBIT: largest V block scale of the call [batch][heads] */
+} fa_io;
+
+typedef struct fa_layout fa_layout; /* opaque, immutable after build */
+
+const char *fa_status_str(fa_status s);
+/* Text of the last failure on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+/*
+ * Validates a descriptor and builds its block map: for every tile of
+ * query rows (one query kind, consecutive rows), the list of key ranges the
+ * rule above makes visible -- ring runs (split at the wrap), the chunk, the
+ * source frames of the tile's rows, the visible reference images -- each
+ * with the mask it needs (none, same-frame, or t0 gate).  Keys outside every
+ * range are never read.  The work order (longest tiles first, heads grouped
+ * per XCD) is fixed here.  Pure host work; the block map goes to the device
+ * on first use.
+ * ring_first_frame: oldest absolute frame the ring holds, or -1 for "all of
+ * [max(0, chunk_start - window), chunk_start)".  Visible history older than
+ * it returns FA_ERR_CAPACITY.
+ * *out receives a new layout owned by the caller (fa_layout_destroy).
+ */
+fa_status fa_layout_build(const fa_layout_desc *d, int32_t ring_first_frame, fa_layout **out);
+
+/*
+ * Work counts of a layout: useful (query, key) pairs and useful FLOPs
+ * (4*head_dim per pair, all heads and batches), keys the kernel visits
+ * (pairs including masked entries of partial tiles), and the algorithmic
+ * HBM bytes (every Q/K/V element read once, O and LSE written once).
+ * Any pointer may be NULL.
+ */
+fa_status fa_layout_stats(const fa_layout *L, double *useful_pairs, double *useful_flops,
+                          double *visited_pairs, double *bytes);
+
+/* Block-map inspection (host).  One query tile and its key ranges. */
+enum { FA_SEG_RING = 0, FA_SEG_TGT = 1, FA_SEG_SRC = 2, FA_SEG_REF = 3 };
+enum { FA_MASK_NONE = 0, FA_MASK_SAME_FRAME = 1, FA_MASK_GATE = 2 };
+typedef struct {
+  int32_t q_kind;   /* 0 target, 1 source, 2 reference rows */
+  int32_t row0;     /* first row of the tile within its query kind */
+  int32_t rows;     /* rows in the tile (the last tile of a kind may be short) */
+  int32_t n_ranges;
+} fa_tile_info;
+typedef struct {
+  int32_t seg;      /* FA_SEG_*: which key tensor */
+  int32_t begin;    /* first key (token index within that tensor) */
+  int32_t end;      /* one past the last key */
+  int32_t mask;     /* FA_MASK_NONE: every row sees every key;
+                       FA_MASK_SAME_FRAME: row of frame f sees keys of frame f only;
+                       FA_MASK_GATE: rows of frame f >= param see the range, others none */
+  int32_t param;    /* FA_MASK_GATE: t0 - chunk_start */
+} fa_range_info;
+fa_status fa_layout_tiles(const fa_layout *L, int32_t *n_tiles, int32_t *block_m, int32_t *block_n);
+/* Copies tile i and up to cap of its ranges. */
+fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile, fa_range_info *ranges,
+                         int32_t cap);
+
+/* Frees a layout (host and device parts).  Work using it must have completed. */
+fa_status fa_layout_destroy(fa_layout *L);
+
+/*
+ * Frame-aligned attention forward for one call described by L: O and LSE
+ * for the rows in L's query_rows, on `stream`.  FA_F32 and FA_BF16 read the
+ * tensors directly; FA_LOWBIT reads the codes and scales written by
+ * fa_quantize_lowbit (q/k int8, v e4m3) and writes bf16 O.  Rows with no
+ * visible key (impossible under the rule unless T = 0) get O = 0, LSE = -inf.
+ * Allocates nothing; asynchronous.
+ */
+fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
+
+/*
+ * Low-bit prologue for an FA_LOWBIT layout.  From the bf16 tensors of `in`:
+ *  - a per-(batch, head) channel mean m of all keys the call reads (ring
+ *    frames in view, chunk, source, references) into out->k_mean, or, with
+ *    FA_QUANT_MEAN_GIVEN, m read from out->k_mean;
+ *  - every Q (query kinds of L) and every key tensor as symmetric int8 per
+ *    (batch, head, 128-token block): scale = absmax/127, code =
+ *    round_half_even(x * (127/absmax)), keys after subtracting m (exact for
+ *    the softmax: q.m is constant along a row);
+ *  - every V as OCP e4m3 per block: scale = absmax/448, round to nearest
+ *    even, saturating; the largest V block scale per (batch, head) into
+ *    out->v_absmax.
+ * Codes go to out->{q,k,v}_* .data (same strides as declared there), scales
+ * to their .scale arrays.  Ring frames outside the call's view are not read.
+ */
+enum { FA_QUANT_MEAN_GIVEN = 1 };
+fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out, int32_t flags,
+                             fa_hip_stream stream);
+
+/*
+ * Streaming append (structured summary section 4.3, sliding-window KV cache;
+ * section 5.2, source frames are not cached): copies frames [0, frames) of
+ * k_chunk/v_chunk -- absolute frames first_frame .. first_frame+frames-1 --
+ * into ring slots (frame mod d->cache_frames).  Element type from d->dtype
+ * (FA_LOWBIT rings hold bf16 and are quantised per call).  Asynchronous.
+ */
+fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const fa_tensor *v_ring,
+                         const fa_tensor *k_chunk, const fa_tensor *v_chunk, int32_t first_frame,
+                         int32_t frames, fa_hip_stream stream);
+
+/*
+ * Streaming driver: one object per stream of chunks.  It keeps the frame
+ * counter and what the ring holds, caches the layout of every distinct
+ * chunk position, and per chunk runs attention over (ring history in the
+ * window, chunk, its source frames, the references) then appends the
+ * chunk's target K/V to the ring.  Source K/V are never kept.
+ */
+typedef struct fa_stream fa_stream;
+/* d gives the chunk geometry; its chunk_start is the first chunk's frame. */
+fa_status fa_stream_create(const fa_layout_desc *d, fa_stream **out);
+/* Attention for the next chunk (fa_attn_fwd with the stream's layout), then
+ * fa_stream_advance.  FA_F32 and FA_BF16 streams. */
+fa_status fa_stream_chunk(fa_stream *s, const fa_io *io, fa_hip_stream stream);
+/* Appends the chunk's target K/V (io->k_tgt/v_tgt) to the ring (io->k_ring/v_ring)
+ * at the next frame position and advances the stream by d->frames.  Low-bit
+ * streams call fa_stream_layout, fa_quantize_lowbit and fa_attn_fwd first. */
+fa_status fa_stream_advance(fa_stream *s, const fa_io *io, fa_hip_stream stream);
+/* The layout the next chunk will use (owned by the stream; valid until destroy). */
+fa_status fa_stream_layout(fa_stream *s, const fa_layout **out);
+/* next_frame: chunk_start of the next chunk; ring_first_frame: oldest frame held
+ * (== next_frame when the ring is empty). */
+fa_status fa_stream_state(const fa_stream *s, int32_t *next_frame, int32_t *ring_first_frame);
+/* Resume at a saved state (the ring tensors must hold what that state says). */
+fa_status fa_stream_seek(fa_stream *s, int32_t next_frame, int32_t ring_first_frame);
+/* Replace the reference set (a reference injected mid-stream with its t0). */
+fa_status fa_stream_set_refs(fa_stream *s, int32_t n_ref, const int32_t *ref_tokens,
+                             const int32_t *ref_t0);
+fa_status fa_stream_destroy(fa_stream *s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

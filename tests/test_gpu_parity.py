@@ -1,0 +1,230 @@
+"""HIP path (libfa.so through the C ABI) against the CPU oracle, element by
+element on the same seeded inputs.  Tolerances on O: fp32 max|d| <= 1e-5;
+bf16 max|d| <= 1e-2 and mean|d| <= 1e-3; plus LSE bounds (1e-4 fp32, 2e-3
+bf16) because under N(0,1) inputs |O| is ~0.01 and an O bound alone would
+not catch a wrong mask."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import gpu_helpers as G
+from frame_aligned_attention_amd import binding as B
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+TGT, SRC, REF = G.TGT, G.SRC, G.REF
+
+
+def workload_call(wid, H=None, C=None, T=None) -> G.Call:
+    """A bidirectional workload as one call (all query kinds)."""
+    w = W.WORKLOADS[wid]
+    H, C, T = H or w.H, C or w.C, T or w.T
+    x = W.chunk_tensors(w, 0, H=H, T=T, C=C, with_queries_src_ref=True)
+    r = W.ref_tensors(w, H=H, with_queries=True)
+    c = G.Call(T=T, C=C, H=H, D=w.D, dtype=w.dtype, ref_tokens=list(w.ref_tokens),
+               ref_t0=list(w.ref_t0), query_rows=7)
+    c.q = {TGT: x["q_tgt"], SRC: x["q_src"], REF: r["q_ref"]}
+    c.k_hist, c.v_hist = x["k_tgt"], x["v_tgt"]
+    c.k_src, c.v_src = x["k_src"], x["v_src"]
+    c.k_ref, c.v_ref = r["k_ref"], r["v_ref"]
+    return c
+
+
+def test_f32_tiny_workload():
+    G.say("case: fp32 tiny workload (T=64, F=2, 16 ref tokens, H=2, D=64)")
+    c = workload_call(0)
+    G.compare_all(c, G.run_call(c), "fp32 tiny")
+
+
+SMALL = [
+    # seed, T, C, H, D, dtype, refs, t0, query_rows
+    (1, 7, 2, 2, 128, "bf16", [3], [0], 7),
+    (2, 24, 3, 2, 128, "bf16", [16, 5], [0, 2], 7),
+    (3, 40, 5, 1, 64, "bf16", [16], [3], 7),
+    (4, 130, 2, 3, 128, "bf16", [9], [1], 7),
+    (5, 64, 1, 2, 128, "bf16", [], [], 7),
+    (6, 200, 3, 2, 128, "bf16", [300, 70], [0, 1], 7),
+    (7, 40, 5, 2, 128, "f32", [16], [3], 7),
+    (8, 33, 4, 2, 64, "f32", [5, 9], [0, 2], 7),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=["s%d" % c[0] for c in SMALL])
+def test_small_shapes(case):
+    seed, T, C, H, D, dt, refs, t0s, qr = case
+    G.say("case: small %s" % (case,))
+    c = G.random_call(seed, T, C, H, D, dt, ref_tokens=refs, ref_t0=t0s, query_rows=qr)
+    G.compare_all(c, G.run_call(c), "small s%d" % seed)
+
+
+STREAMS = [
+    # seed, T, C, H, D, cs, window, cache, refs, t0
+    (11, 50, 3, 2, 128, 9, 4, 5, [20], [0]),         # ring wraps
+    (12, 50, 3, 2, 128, 12, 4, 5, [20], [0]),
+    (13, 30, 3, 2, 128, 12, 9, 9, [10, 7], [0, 13]),  # t0 gate inside the chunk
+    (14, 33, 2, 1, 64, 3, 12, 12, [5], [40]),        # warm-up, reference not yet visible
+    (15, 17, 3, 2, 128, 6, -1, 9, [4], [0]),         # all history
+    (16, 100, 3, 2, 128, 3, 0, 4, [200], [0]),       # window 0
+]
+
+
+@pytest.mark.parametrize("case", STREAMS, ids=["st%d" % c[0] for c in STREAMS])
+def test_streaming_calls(case):
+    seed, T, C, H, D, cs, win, cap, refs, t0s = case
+    G.say("case: streaming %s" % (case,))
+    c = G.random_call(seed, T, C, H, D, "bf16", cs=cs, window=win, cache=cap, ref_tokens=refs,
+                      ref_t0=t0s, query_rows=3)
+    G.compare_all(c, G.run_call(c), "stream st%d" % seed)
+
+
+def test_bidirectional_reduced():
+    G.say("case: bidirectional bf16, F=3, T=1560, H=2, all rows, full oracle")
+    c = workload_call(1, H=2, C=3)
+    G.compare_all(c, G.run_call(c), "bidir reduced")
+
+
+def test_bidirectional_full_size_sampled():
+    G.say("case: bidirectional bf16 full size (F=21, T=1560, H=12), sampled rows")
+    c = workload_call(1)
+    res = G.run_call(c)
+    G.compare_sampled(c, res, n_rows=48, heads=[0, 7, 11], what="bidir full")
+
+
+def test_bidirectional_full_size_q_zero_closed_form():
+    """Q = 0: O is the mean of the visible V rows and LSE = ln(#visible) at full size."""
+    G.say("case: bidirectional bf16 full size, Q = 0 closed form")
+    c = workload_call(1)
+    for k in c.q:
+        c.q[k] = np.zeros_like(c.q[k])
+    res = G.run_call(c)
+    T, C = c.T, c.C
+    vt, vs, vr = (c.v_hist.astype(np.float64), c.v_src.astype(np.float64),
+                  c.v_ref.astype(np.float64))
+    sum_t, sum_r = vt.sum(0), vr.sum(0)
+    for f in (0, 1, 10, 20):
+        n_t = C * T + T + sum(c.ref_tokens)
+        mean_t = (sum_t + vs[f * T:(f + 1) * T].sum(0) + sum_r) / n_t
+        o, lse = res[TGT]
+        rows = [f * T, f * T + 777, f * T + T - 1]
+        G.tol_check(o[rows], np.broadcast_to(mean_t, (3,) + mean_t.shape), "bf16",
+                    "Q=0 target frame %d" % f, lse[:, rows], np.full((c.H, 3), math.log(n_t)))
+        n_s = T + sum(c.ref_tokens)
+        mean_s = (vs[f * T:(f + 1) * T].sum(0) + sum_r) / n_s
+        o, lse = res[SRC]
+        G.tol_check(o[rows], np.broadcast_to(mean_s, (3,) + mean_s.shape), "bf16",
+                    "Q=0 source frame %d" % f, lse[:, rows], np.full((c.H, 3), math.log(n_s)))
+    o, lse = res[REF]
+    G.tol_check(o[[0, 1559]], np.broadcast_to(sum_r / 1560, (2,) + sum_r.shape), "bf16",
+                "Q=0 reference rows", lse[:, [0, 1559]], np.full((c.H, 2), math.log(1560)))
+
+
+def stream_call(wid, cs, H=None) -> G.Call:
+    """One chunk of a streaming workload with its history (chunk seeds by frame // C)."""
+    w = W.WORKLOADS[wid]
+    H = H or w.H
+    lo = max(0, cs - w.window)
+    c = G.Call(T=w.T, C=w.C, H=H, D=w.D, dtype="bf16", cs=cs, window=w.window,
+               cache=w.cache_frames, ref_tokens=list(w.ref_tokens), ref_t0=w.t0_for(cs),
+               query_rows=1, hist_first=lo)
+    ks, vs = [], []
+    for ch in range(lo // w.C, cs // w.C + 1):
+        x = W.chunk_tensors(w, ch, H=H)
+        ks.append(x["k_tgt"]); vs.append(x["v_tgt"])
+    first = (lo // w.C) * w.C
+    off = (lo - first) * w.T
+    c.k_hist = np.concatenate(ks)[off:]
+    c.v_hist = np.concatenate(vs)[off:]
+    x = W.chunk_tensors(w, cs // w.C, H=H)
+    r = W.ref_tensors(w, H=H)
+    c.q = {TGT: x["q_tgt"]}
+    c.k_src, c.v_src = x["k_src"], x["v_src"]
+    c.k_ref, c.v_ref = r["k_ref"], r["v_ref"]
+    return c
+
+
+def test_high_res_chunk_full_size_sampled():
+    G.say("case: 3600-token chunk at cs=12, window 9, two references (t0 = 0, cs+1), H=24")
+    c = stream_call(3, 12)
+    res = G.run_call(c)
+    G.compare_sampled(c, res, n_rows=64, heads=[0, 23], what="hi-res chunk")
+
+
+def test_high_res_chunk_reduced_full_oracle():
+    G.say("case: 3600-token chunk, H=1, every row against the oracle")
+    c = stream_call(3, 12, H=1)
+    G.compare_all(c, G.run_call(c), "hi-res chunk H=1")
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+
+def test_source_perturbation_is_local():
+    """Perturbing source frame j leaves target rows of every other frame bit-identical."""
+    G.say("case: source-frame perturbation (bf16, T=200, C=4)")
+    c = G.random_call(21, 200, 4, 2, 128, "bf16", ref_tokens=[50], ref_t0=[0], query_rows=3)
+    base = G.run_call(c)
+    g = np.random.default_rng(5)
+    for j in (0, 2):
+        c2 = G.random_call(21, 200, 4, 2, 128, "bf16", ref_tokens=[50], ref_t0=[0], query_rows=3)
+        c2.k_src[j * 200:(j + 1) * 200] = W.round_bf16(g.standard_normal((200, 2, 128)) * 3)
+        c2.v_src[j * 200:(j + 1) * 200] = W.round_bf16(g.standard_normal((200, 2, 128)) * 3)
+        res = G.run_call(c2)
+        for t in range(4):
+            sl = slice(t * 200, (t + 1) * 200)
+            same = np.array_equal(res[TGT][0][sl], base[TGT][0][sl]) and np.array_equal(
+                res[TGT][1][:, sl], base[TGT][1][:, sl])
+            assert same == (t != j), (t, j)
+
+
+def test_nan_poison_outside_ranges():
+    """Ring slots outside the window and output padding hold NaN: results stay finite and
+    equal to the clean run."""
+    G.say("case: NaN poison in ring slots the block map does not cover")
+    c = G.random_call(22, 50, 3, 2, 128, "bf16", cs=12, window=4, cache=7, ref_tokens=[20],
+                      ref_t0=[0], query_rows=1)
+    clean = G.run_call(c, poison=0.0)
+    dirty = G.run_call(c, poison=float("nan"))
+    o, lse = dirty[TGT]
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert np.array_equal(o, clean[TGT][0]) and np.array_equal(lse, clean[TGT][1])
+
+
+def test_run_to_run_deterministic():
+    G.say("case: determinism (two runs bit-identical)")
+    c = workload_call(1, H=2, C=3)
+    a = G.run_call(c)
+    b = G.run_call(c, out_fill=float("nan"))
+    for k in a:
+        assert np.array_equal(a[k][0], b[k][0]) and np.array_equal(a[k][1], b[k][1])
+
+
+def test_strided_and_batched_inputs():
+    """Q/K/V as views into packed [B, N, 3, H, D] buffers, batch 2: same as separate calls."""
+    G.say("case: strided views and batch 2")
+    T, C, H, D = 40, 3, 2, 128
+    calls = [G.random_call(30 + b, T, C, H, D, "bf16", ref_tokens=[24], ref_t0=[1],
+                           query_rows=7) for b in range(2)]
+    N = C * T
+    packed = {}
+    for name, src in (("tgt", lambda c: (c.q[TGT], c.k_hist, c.v_hist)),
+                      ("src", lambda c: (c.q[SRC], c.k_src, c.v_src)),
+                      ("ref", lambda c: (c.q[REF], c.k_ref, c.v_ref))):
+        arr = np.stack([np.stack(src(c), 1) for c in calls])  # [B, N, 3, H, D]
+        packed[name] = torch.from_numpy(arr).to("cuda").to(torch.bfloat16)
+    t = {}
+    for name in ("tgt", "src", "ref"):
+        p = packed[name]
+        t["q_" + name], t["k_" + name], t["v_" + name] = p[:, :, 0], p[:, :, 1], p[:, :, 2]
+        rows = p.shape[1]
+        t["o_" + name] = torch.zeros((2, rows, H, D), dtype=torch.bfloat16, device="cuda")
+        t["lse_" + name] = torch.zeros((2, H, rows), dtype=torch.float32, device="cuda")
+    d = B.make_desc(C, T, H, D, batch=2, ref_tokens=[24], ref_t0=[1], query_rows=7)
+    B.fa_attn_fwd(B.fa_layout_build(d), B.make_io(t))
+    torch.cuda.synchronize()
+    for b, c in enumerate(calls):
+        single = G.run_call(c)
+        for k, nm in ((TGT, "tgt"), (SRC, "src"), (REF, "ref")):
+            assert np.array_equal(G.host(t["o_" + nm][b]), single[k][0]), (b, nm)
+            assert np.array_equal(G.host(t["lse_" + nm][b]), single[k][1]), (b, nm)

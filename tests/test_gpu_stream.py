@@ -1,0 +1,135 @@
+"""Streaming driver (fa_stream_*) on the GPU: a 20-chunk stream of the
+1560-token workload (reduced heads) through the ring-buffer KV cache against
+the oracle, ring contents, reference injection mid-stream, and
+checkpoint/resume."""
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import gpu_helpers as G
+from frame_aligned_attention_amd import binding as B
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+TGT = G.TGT
+
+
+class StreamRun:
+    """Drives fa_stream over seeded chunks of workload `wid` with `H` heads."""
+
+    def __init__(self, wid, H):
+        self.w = W.WORKLOADS[wid]
+        w = self.w
+        self.H = H
+        self.desc = B.make_desc(w.C, w.T, H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
+                                chunk_start=0, window=w.window, cache_frames=w.cache_frames,
+                                query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16)
+        self.s = B.Stream(self.desc)
+        z = lambda: torch.zeros((1, w.cache_frames * w.T, H, w.D), dtype=torch.bfloat16,
+                                device="cuda")
+        self.k_ring, self.v_ring = z(), z()
+        r = W.ref_tensors(w, H=H)
+        self.ref = {"k_ref": G.dev(r["k_ref"]), "v_ref": G.dev(r["v_ref"])}
+        self.ref_host = r
+        self.k_all, self.v_all = [], []  # host target K/V by chunk
+
+    def chunk_inputs(self, ch):
+        x = W.chunk_tensors(self.w, ch, H=self.H)
+        return x
+
+    def run_chunk(self, ch):
+        w = self.w
+        x = self.chunk_inputs(ch)
+        t = {"q_tgt": G.dev(x["q_tgt"]), "k_tgt": G.dev(x["k_tgt"]), "v_tgt": G.dev(x["v_tgt"]),
+             "k_src": G.dev(x["k_src"]), "v_src": G.dev(x["v_src"]),
+             "k_ring": self.k_ring, "v_ring": self.v_ring, **self.ref}
+        rows = w.C * w.T
+        t["o_tgt"] = torch.empty((1, rows, self.H, w.D), dtype=torch.bfloat16, device="cuda")
+        t["lse_tgt"] = torch.empty((1, self.H, rows), dtype=torch.float32, device="cuda")
+        self.s.chunk(B.make_io(t))
+        torch.cuda.synchronize()
+        self.k_all.append(x["k_tgt"])
+        self.v_all.append(x["v_tgt"])
+        return x, G.host(t["o_tgt"])[0], G.host(t["lse_tgt"])[0]
+
+    def oracle_call(self, ch, x, ref_t0=None):
+        w = self.w
+        cs = ch * w.C
+        lo = max(0, cs - w.window)
+        c = G.Call(T=w.T, C=w.C, H=self.H, D=w.D, dtype="bf16", cs=cs, window=w.window,
+                   cache=w.cache_frames, ref_tokens=list(w.ref_tokens),
+                   ref_t0=list(ref_t0 if ref_t0 is not None else w.ref_t0), query_rows=1,
+                   hist_first=lo)
+        kh = np.concatenate(self.k_all[lo // w.C:])
+        vh = np.concatenate(self.v_all[lo // w.C:])
+        off = (lo - (lo // w.C) * w.C) * w.T
+        c.k_hist, c.v_hist = kh[off:], vh[off:]
+        c.q = {TGT: x["q_tgt"]}
+        c.k_src, c.v_src = x["k_src"], x["v_src"]
+        c.k_ref, c.v_ref = self.ref_host["k_ref"], self.ref_host["v_ref"]
+        return c
+
+
+def test_stream_20_chunks_against_oracle():
+    G.say("case: 20-chunk stream, T=1560, C=3, window 12, ring 12, H=2")
+    run = StreamRun(2, H=2)
+    for ch in range(20):
+        x, o, lse = run.run_chunk(ch)
+        c = run.oracle_call(ch, x)
+        if ch in (0, 4, 19):
+            c1 = run.oracle_call(ch, x)
+            ref = O.attn(c1.problem(), kinds=(TGT,))[TGT]
+            G.tol_check(o, ref[0], "bf16", "chunk %d all rows" % ch, lse, ref[1])
+        else:
+            G.compare_sampled(c, {TGT: (o, lse)}, n_rows=24, what="chunk %d" % ch)
+    # ring holds frames 48..59 in slots f % 12, bit-exact
+    w = run.w
+    kr = G.host(run.k_ring)[0]
+    for f in range(48, 60):
+        s = f % 12
+        want = run.k_all[f // 3][(f % 3) * w.T:(f % 3 + 1) * w.T]
+        assert np.array_equal(kr[s * w.T:(s + 1) * w.T], want), f
+    assert run.s.state() == (60, 48)
+
+
+def test_stream_checkpoint_resume_bit_identical():
+    G.say("case: checkpoint after chunk 7, resume, chunks 8..11 bit-identical")
+    a = StreamRun(2, H=1)
+    outs = {}
+    for ch in range(12):
+        _, o, lse = a.run_chunk(ch)
+        if ch == 7:
+            saved_k, saved_v = a.k_ring.clone(), a.v_ring.clone()
+            state = a.s.state()
+        if ch >= 8:
+            outs[ch] = (o, lse)
+    b = StreamRun(2, H=1)
+    b.s.seek(*state)
+    b.k_ring.copy_(saved_k)
+    b.v_ring.copy_(saved_v)
+    for ch in range(8, 12):
+        _, o, lse = b.run_chunk(ch)
+        assert np.array_equal(o, outs[ch][0]) and np.array_equal(lse, outs[ch][1]), ch
+
+
+def test_stream_reference_injected_mid_stream():
+    G.say("case: reference image injected at frame 10 (t0 = 10)")
+    run = StreamRun(2, H=1)
+    w = run.w
+    g = np.random.default_rng(77)
+    k2 = W.round_bf16(g.standard_normal((300, 1, w.D), dtype=np.float32))
+    v2 = W.round_bf16(g.standard_normal((300, 1, w.D), dtype=np.float32))
+    for ch in range(6):
+        if ch == 3:  # inject before the chunk at cs = 9: frame 9 must not see it, 10 and 11 must
+            run.s.set_refs([1560, 300], [0, 10])
+            run.ref = {"k_ref": G.dev(np.concatenate([run.ref_host["k_ref"], k2])),
+                       "v_ref": G.dev(np.concatenate([run.ref_host["v_ref"], v2]))}
+            run.ref_host = {"k_ref": np.concatenate([run.ref_host["k_ref"], k2]),
+                            "v_ref": np.concatenate([run.ref_host["v_ref"], v2])}
+            run.w = W.Workload(**{**run.w.__dict__, "ref_tokens": [1560, 300],
+                                  "ref_t0": [0, 10]})
+        x, o, lse = run.run_chunk(ch)
+        if ch >= 2:
+            c = run.oracle_call(ch, x)
+            G.compare_sampled(c, {TGT: (o, lse)}, n_rows=40, what="inject chunk %d" % ch)

@@ -1,0 +1,212 @@
+"""Block map (fa_layout_build) against the oracle's visibility.  CPU only.
+
+For every query row of small layouts -- unaligned frame sizes against the
+kernels' 64/128-row tiles, ring wrap, gated references, all three query
+kinds -- the keys the block map hands to the kernel (ranges filtered by their
+masks) must be exactly the keys the oracle finds visible, each once.  For the
+workload-sized layouts the per-row key counts are compared on sampled rows,
+and the useful-FLOP totals against the oracle's counts.
+"""
+import numpy as np
+import pytest
+
+import fa_workloads as W
+from frame_aligned_attention_amd import binding as B
+from oracle import oracle as O
+
+TGT, SRC, REF = O.FAO_TGT, O.FAO_SRC, O.FAO_REF
+
+
+def blockmap_columns(L, d, ring_first, ref_total):
+    """{kind: list over rows of the visited key columns} in the oracle's key order
+    (target frames 0 .. cs+C-1, then source frames, then reference tokens)."""
+    T, C, cs, cap = d.tokens_per_frame, d.frames, d.chunk_start, d.cache_frames
+    nhist = (cs + C) * T
+    nsrc = C * T
+    held = {g % cap: g for g in range(ring_first, cs)} if cap else {}
+    n, bm, bn = B.fa_layout_tiles(L)
+    out = {}
+    for i in range(n):
+        (kind, row0, rows), ranges = B.fa_layout_tile(L, i)
+        total = {0: C * T, 1: C * T, 2: ref_total}[kind]
+        lst = out.setdefault(kind, [None] * total)
+        for row in range(row0, row0 + rows):
+            cols = []
+            fq = row // T
+            for seg, beg, end, mask, param in ranges:
+                for k in range(beg, end):
+                    if mask == B.FA_MASK_SAME_FRAME and k // T != fq:
+                        continue
+                    if mask == B.FA_MASK_GATE and fq < param:
+                        continue
+                    if seg == B.FA_SEG_RING:
+                        assert k // T in held, "range covers ring slot %d not held" % (k // T)
+                        cols.append(held[k // T] * T + k % T)
+                    elif seg == B.FA_SEG_TGT:
+                        cols.append(cs * T + k)
+                    elif seg == B.FA_SEG_SRC:
+                        cols.append(nhist + k)
+                    else:
+                        cols.append(nhist + nsrc + k)
+            assert lst[row] is None, "row %d in two tiles" % row
+            lst[row] = cols
+    return out
+
+
+def oracle_visibility(d, refs, t0s):
+    T, C, cs = d.tokens_per_frame, d.frames, d.chunk_start
+    nh, ns, R = (cs + C) * T, C * T, sum(refs)
+    nk = nh + ns + R
+    eye = np.eye(nk, dtype=np.float32)[:, None, :]
+    z = lambda n: np.zeros((n, 1, nk), np.float32)
+    g = np.random.default_rng(1)
+    k = lambda n: g.standard_normal((n, 1, nk)).astype(np.float32)
+    p = O.Problem(T=T, C=C, H=1, D=nk, cs=cs, window=d.window, hist_first=0, ref_tokens=refs,
+                  ref_t0=t0s, q_tgt=z(ns), q_src=z(ns), q_ref=z(R), k_hist=k(nh),
+                  v_hist=eye[:nh], k_src=k(ns), v_src=eye[nh:nh + ns], k_ref=k(R),
+                  v_ref=eye[nh + ns:])
+    res = O.attn(p)
+    return {kind: res[kind][0][:, 0, :] > 0 for kind in res}
+
+
+SMALL = [
+    # frames, T, refs, t0, cs, window, cap, ring_first(-1 default), query_rows, dtype
+    (2, 7, [3], [0], 0, 0, 0, -1, 7, B.FA_BF16),
+    (3, 24, [16, 5], [0, 2], 0, 0, 0, -1, 7, B.FA_BF16),
+    (5, 40, [16], [3], 0, 0, 0, -1, 7, B.FA_F32),
+    (1, 64, [16], [0], 0, 0, 0, -1, 7, B.FA_F32),
+    (2, 64, [], [], 0, 0, 0, -1, 7, B.FA_F32),
+    (3, 50, [20], [0], 9, 4, 5, -1, 1, B.FA_BF16),     # ring wraps: frames 5..8 in slots 0..3
+    (3, 50, [20], [0], 12, 4, 5, -1, 3, B.FA_BF16),    # frames 8..11 -> slots 3,4,0,1
+    (3, 30, [10, 7], [0, 13], 12, 9, 9, -1, 1, B.FA_BF16),  # gate splits the chunk
+    (3, 30, [10, 7], [0, 13], 12, 9, 9, 3, 1, B.FA_LOWBIT),
+    (2, 33, [5], [40], 3, 12, 12, 0, 1, B.FA_BF16),    # warm-up: window > history; ref never
+    (3, 17, [4], [0], 6, -1, 8, 0, 3, B.FA_BF16),      # all history
+    (2, 130, [9], [1], 0, 0, 0, -1, 7, B.FA_BF16),     # tiles across frame boundaries
+    (3, 60, [200], [0], 3, 0, 4, -1, 7, B.FA_BF16),    # window 0: no history; 3 frames a tile
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(i) for i in range(len(SMALL))])
+def test_blockmap_equals_oracle_visibility(case):
+    F, T, refs, t0s, cs, win, cap, rf, qr, dt = case
+    hd = 128
+    d = B.make_desc(F, T, 1, hd, ref_tokens=refs, ref_t0=t0s, chunk_start=cs, window=win,
+                    cache_frames=cap, query_rows=qr, dtype=dt)
+    L = B.fa_layout_build(d, rf)
+    lo = 0 if win < 0 else max(0, cs - win)
+    ring_first = rf if rf >= 0 else (lo if lo < cs else cs)
+    cols = blockmap_columns(L, d, ring_first, sum(refs))
+    vis = oracle_visibility(d, refs, t0s)
+    kinds = [k for k, bit in ((TGT, 1), (SRC, 2), (REF, 4)) if qr & bit]
+    useful = 0
+    for kind in kinds:
+        want = vis[kind]
+        got_rows = cols.get(kind, [])
+        assert len(got_rows) == want.shape[0] or want.shape[0] == 0
+        for row, c in enumerate(got_rows):
+            assert c is not None, "row %d of kind %d in no tile" % (row, kind)
+            assert len(c) == len(set(c)), "a key visited twice (kind %d row %d)" % (kind, row)
+            got = np.zeros(want.shape[1], bool)
+            got[c] = True
+            assert np.array_equal(got, want[row]), (kind, row, np.nonzero(got != want[row]))
+            useful += len(c)
+    st = B.fa_layout_stats(L)
+    assert st["useful_pairs"] == useful
+    assert st["useful_flops"] == useful * 4 * hd
+    assert st["visited_pairs"] >= useful
+
+
+def test_tile_rows_and_sizes():
+    d = B.make_desc(21, 1560, 12, 128, ref_tokens=[1560], ref_t0=[0], query_rows=7)
+    L = B.fa_layout_build(d)
+    n, bm, bn = B.fa_layout_tiles(L)
+    assert (bm, bn) == (128, 64)
+    assert n == 256 + 256 + 13  # 32760 = 255*128 + 120 rows per kind, 1560 reference rows
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 255)
+    assert (kind, row0, rows) == (0, 255 * 128, 120)
+    # frame boundary tile: rows 1536..1663 cover frames 0 and 1 -> same-frame source range
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 12)
+    assert (row0, rows) == (1536, 128)
+    assert (B.FA_SEG_SRC, 0, 2 * 1560, B.FA_MASK_SAME_FRAME, 0) in ranges
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 11)
+    assert (B.FA_SEG_SRC, 0, 1560, B.FA_MASK_NONE, 0) in ranges
+
+
+def workload_layout(wid, cs=None):
+    w = W.WORKLOADS[wid]
+    if w.streaming:
+        cs = w.first_cs if cs is None else cs
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.t0_for(cs),
+                        chunk_start=cs, window=w.window, cache_frames=w.cache_frames,
+                        query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16)
+    else:
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
+                        query_rows=7, dtype=B.FA_F32 if w.dtype == "f32" else B.FA_BF16)
+    return w, d, B.fa_layout_build(d)
+
+
+def oracle_counts(w, d):
+    """Useful pairs per head from the oracle's per-row counts (one row per frame)."""
+    cs = d.chunk_start
+    p = O.Problem(T=w.T, C=w.C, H=1, D=1, cs=cs, window=d.window if w.streaming else -1,
+                  hist_first=0, ref_tokens=w.ref_tokens, ref_t0=list(d.ref_t0)[:len(w.ref_tokens)])
+    total = 0
+    kinds = [TGT] if w.streaming else [TGT, SRC, REF]
+    for kind in kinds:
+        if kind == REF:
+            total += sum(w.ref_tokens) * O.count(p, REF, 0)
+            continue
+        for f in range(w.C):
+            total += w.T * O.count(p, kind, f * w.T)
+    return total
+
+
+@pytest.mark.parametrize("wid,cs,want_per_head", [
+    (0, None, 37120),
+    (1, None, 1280073600),
+    (2, 57, 124113600),
+    (2, 0, None),
+    (2, 6, None),
+    (3, 12, 570240000),
+])
+def test_workload_useful_pairs(wid, cs, want_per_head):
+    w, d, L = workload_layout(wid, cs)
+    st = B.fa_layout_stats(L)
+    per_head = st["useful_pairs"] / w.H
+    assert per_head == oracle_counts(w, d)
+    if want_per_head is not None:
+        assert per_head == want_per_head
+    # sampled rows: map coverage per row equals the oracle count
+    n, bm, bn = B.fa_layout_tiles(L)
+    p = O.Problem(T=w.T, C=w.C, H=1, D=1, cs=d.chunk_start,
+                  window=d.window if w.streaming else -1, hist_first=0,
+                  ref_tokens=w.ref_tokens, ref_t0=list(d.ref_t0)[:len(w.ref_tokens)])
+    for i in range(0, n, max(1, n // 23)):
+        (kind, row0, rows), ranges = B.fa_layout_tile(L, i)
+        for row in (row0, row0 + rows - 1):
+            fq = row // w.T
+            cnt = 0
+            for seg, beg, end, mask, param in ranges:
+                if mask == B.FA_MASK_SAME_FRAME:
+                    cnt += max(0, min(end, (fq + 1) * w.T) - max(beg, fq * w.T))
+                elif mask == B.FA_MASK_GATE:
+                    cnt += (end - beg) if fq >= param else 0
+                else:
+                    cnt += end - beg
+            assert cnt == O.count(p, kind, row), (i, row)
+
+
+def test_stream_layout_sequence():
+    """The stream object's layouts over the 20 chunks of the 1560x40-head stream."""
+    w = W.WORKLOADS[2]
+    d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=0,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=1)
+    s = B.Stream(d)
+    keys = []
+    for cs in W.stream_chunk_starts(w):
+        s.seek(cs, max(0, cs - w.cache_frames))
+        st = B.fa_layout_stats(s.layout())
+        keys.append(st["useful_pairs"] / w.H / (w.C * w.T))
+    assert keys[:5] == [7800, 12480, 17160, 21840, 26520]
+    assert all(k == 26520 for k in keys[4:])
