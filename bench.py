@@ -212,7 +212,7 @@ def cpu_baseline(W, budget_s):
     n = 64
     done_rows, spent = 0, 0.0
     g = np.random.default_rng(0)
-    while spent < budget_s and done_rows < rows_total:
+    while spent < budget_s and done_rows < 64 * rows_total:
         rows = g.integers(0, rows_total, size=n)
         t0 = time.perf_counter()
         O.attn_rows(p, [O.FAO_TGT] * n, [0] * n, rows.tolist())
@@ -234,6 +234,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other bf16 workloads")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the attention "
@@ -246,6 +248,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_check:
+        n = args.copy_check * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("bench: copy check %d MiB read + %d MiB written" % (args.copy_check, args.copy_check))
+        del a, b
     res = run_stream_bench(args, torch, W, B)
     w = res["w"]
     value = res["useful"] / res["total_ms"] / 1e9  # TFLOP/s

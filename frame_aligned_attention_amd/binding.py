@@ -57,11 +57,25 @@ class fa_range_info(C.Structure):
                 ("param", C.c_int32)]
 
 
+def _hip_runtimes():
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return set()
+    return {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libfa.so is not built (%s); run __graft_entry__.build() or "
                           "python frame_aligned_attention_amd/build.py" % LIB_PATH)
+    # torch first: libfa.so must bind to the HIP runtime torch already loaded (same soname),
+    # so that torch's device pointers and streams are valid in the library.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
+    if len(_hip_runtimes()) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s); libfa.so must share torch's"
+                          % sorted(_hip_runtimes()))
     P = C.c_void_p
     sig = {
         "fa_status_str": ([C.c_int], C.c_char_p),
