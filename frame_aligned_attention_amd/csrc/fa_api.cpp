@@ -89,6 +89,13 @@ static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t strea
     if (st != FA_OK) return st;
     st = check_tensor(*vs[s], eq, d.batch, kVName[s], low);
     if (st != FA_OK) return st;
+    if (d.dtype != FA_F32) {
+      // the tiled kernels bound each key tile with a buffer descriptor over whole rows
+      for (const fa_tensor *t : {ks[s], vs[s]})
+        if (t->stride_n < d.head_dim || t->stride_n > (1 << 24))
+          return fail(FA_ERR_UNSUPPORTED, std::string(kKName[s]) +
+                                              "/v: stride_n must be in [head_dim, 2^24]");
+    }
     a.k[s] = seg_of(*ks[s], seg_tok[s]);
     a.v[s] = seg_of(*vs[s], seg_tok[s]);
   }

@@ -10,30 +10,47 @@
 // Each wave owns 32 query rows and computes, per key tile,
 //   S^T (64 keys x 32 queries) = K_tile . Q^T   with v_mfma_f32_32x32x16_bf16,
 // so every lane holds one query column and 32 of its scores: the row max and
-// row sum are in-lane, plus one v_permlane32_swap between the two lane halves.
-// Then O^T (D x 32) += V^T_tile . P^T, again 32x32x16 MFMAs; P never leaves
-// registers because the S^T accumulator already has the B-operand layout of
-// the second product, provided V^T is laid out in LDS in the matching key
-// order (done when the V tile is staged).
+// row sum are in-lane, plus one v_permlane32_swap between the lane halves.
+// Then O^T (D x 32) += V^T_tile . P^T, again 32x32x16 MFMAs.  P never leaves
+// registers: the S^T accumulator already is the B operand of the second
+// product once V^T's key order matches it.
 //
-// Memory.  K and V tiles are double-buffered in LDS (one barrier per tile);
-// the next tile's global loads are issued before the current tile's MFMAs.
-// K rows are padded to keep the 16-byte MFMA-operand reads conflict-free;
-// V is stored transposed (rows = head_dim channels).  Q stays in VGPRs.
+// Memory.  K and V tiles go from HBM straight into LDS (buffer loads with
+// the LDS bit, 16 bytes per lane, no VGPR staging); the buffer descriptor of
+// a tile covers only the keys of its range, so the hardware's bounds check
+// returns zeros for the tail of a partial tile and nothing outside a range
+// is read.  Rows are XOR-swizzled in 16-byte chunks so the MFMA operand
+// reads are free of bank conflicts.  V stays row-major (keys x channels) in
+// LDS and is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16),
+// which hands each lane the 4 keys of one channel its A operand needs.
+//
+// Pipeline.  K tile j+2 and V tile j+1 load while the waves compute
+// softmax(S_j), S_{j+1} = K_{j+1} Q^T and O += V_j P_j; one barrier per
+// tile.  The MFMAs of S_{j+1} do not depend on the softmax of tile j, so
+// the instruction stream interleaves them (matrix core and VALU overlap).
 //
 // Softmax.  Base-2 online softmax with scale*log2(e) folded into one FMA
-// before v_exp_f32.  The running max is only raised when a tile's max
+// before v_exp_f32.  The running max is raised only when a tile's max
 // exceeds it by more than 8 (so p <= 2^8): the O/l rescale is then rare.
+// Row sums are taken on the bf16-rounded p that feed the PV product
+// (v_dot2c_f32_bf16 against ones).
 #include "fa_internal.h"
 
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Raw buffer descriptor word 3 for gfx9-family loads (32-bit data, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float xhalf_max(float x) {
-  // v_permlane32_swap exchanges lanes 32..63 of one operand with lanes 0..31 of the other;
-  // with both operands = x, the pair holds the two halves' values in every lane.
+  // v_permlane32_swap with both operands = x leaves, in every lane, the pair
+  // (x of lane l%32, x of lane 32 + l%32).
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -43,129 +60,104 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = kBf16BlockM;        // 128 rows, 4 waves
-  static constexpr int BN = kBf16BlockN;        // 64 keys per tile
-  static constexpr int KSTR = D * 2 + 16;       // LDS bytes per K row
-  static constexpr int VSTR = BN * 2 + 16;      // LDS bytes per V^T row
-  static constexpr int KBYTES = BN * KSTR;
-  static constexpr int BUF = KBYTES + D * VSTR; // one K+V^T buffer
-  static constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per thread
-  static constexpr int VTASKS = (D / 4) * 8;    // V staging tasks (4 channels x 8 keys each)
+  static constexpr int BN = kBf16BlockN;        // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per K/V row in LDS
+  static constexpr int CH = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
+  static constexpr int LOADS = TILEB / (256 * 16);  // 16-byte direct loads per thread per tile
+  static constexpr int DS = D / 16;             // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;             // 32-channel blocks of O^T
+  // K: chunk c of row r lives at chunk c ^ (r % CH); V: at c ^ ((2r) % CH).  Both keep the
+  // MFMA operand reads (ds_read_b128 over 16 rows; ds_read_b64_tr_b16 over 4 rows x 2 chunks)
+  // on distinct banks.
+  __device__ static int ksw(int r) { return r & (CH - 1); }
+  __device__ static int vsw(int r) { return (2 * r) & (CH - 1); }
 };
+
+// Where each lane's direct loads of a tile land and which bytes of the tile's
+// rows they fetch: load j of wave w writes LDS chunks [(4j + w)*64, +64) of the
+// tile, lane i chunk (4j + w)*64 + i.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_map(int j, int w, int lane, int &row, int &lcb) {
+  using Cfg = Bf16Cfg<D>;
+  const int p = (4 * j + w) * 64 + lane;
+  row = p / Cfg::CH;
+  const int pc = p % Cfg::CH;
+  const int lc = pc ^ (IS_V ? Cfg::vsw(row) : Cfg::ksw(row));
+  lcb = lc * 16;
+}
 
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   using Cfg = Bf16Cfg<D>;
-  constexpr int BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR, BUF = Cfg::BUF;
+  constexpr int BN = Cfg::BN, ROWB = Cfg::ROWB, TILEB = Cfg::TILEB;
   constexpr float kThr = 8.0f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
 
   const DevWork w = a.work[blockIdx.x];
   if (w.tile < 0) return;
   const DevTile tile = a.tiles[w.tile];
   const int b = w.bh / a.H, h = w.bh - (w.bh / a.H) * a.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  // the wave index is uniform per wave; say so, since it feeds M0 (LDS address of direct loads)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int T = a.T;
 
   // ---- Q (B operand of S^T): lane holds query row l32 of its wave, channels ds*16 + 8*hl + 0..7
   const int qloc = wave * 32 + l32;
   const bool qvalid = qloc < tile.rows;
   const int qrow = tile.row0 + qloc;
-  const Seg qs = a.q[tile.q_kind];
-  bf16x8_t qreg[D / 16];
+  bf16x8_t qreg[Cfg::DS];
   {
+    const Seg qs = a.q[tile.q_kind];
     const __bf16 *qp = (const __bf16 *)qs.p + b * qs.sb + (int64_t)qrow * qs.sn + h * qs.sh;
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      if (qvalid)
-        qreg[ds] = *(const bf16x8_t *)(qp + ds * 16 + 8 * hl);
-      else
-        qreg[ds] = bf16x8_t{};
-    }
+    for (int ds = 0; ds < Cfg::DS; ++ds)
+      qreg[ds] = qvalid ? *(const bf16x8_t *)(qp + ds * 16 + 8 * hl) : bf16x8_t{};
   }
   const int fq = qrow / T;  // row frame relative to the chunk (target and source rows)
 
-  // ---- flattened walk over (range, key tile)
+  // ---- per-lane constants of the LDS reads
+  // K (A operand of S^T): row kb*32 + l32, logical chunk 2*ds + hl.
+  int koff[Cfg::DS];
+#pragma unroll
+  for (int ds = 0; ds < Cfg::DS; ++ds)
+    koff[ds] = l32 * ROWB + (((2 * ds + hl) ^ Cfg::ksw(l32)) * 16);
+  // V (A operand of O^T via the transposing read): lane i = 4s + av of 16-lane group g reads
+  // row ks*16 + r*8 + 4*(g/2) + s, channels db*32 + (g%2)*16 + 4*av .. +3.
+  int voff[Cfg::DB];
+  {
+    const int i = lane & 15, g = lane >> 4;
+    const int s = i >> 2, av = i & 3, hv = g >> 1, gh = g & 1;
+    const int vrow = 4 * hv + s;
+#pragma unroll
+    for (int db = 0; db < Cfg::DB; ++db) {
+      const int lc = db * 4 + gh * 2 + (av >> 1);
+      voff[db] = vrow * ROWB + ((lc ^ Cfg::vsw(vrow)) * 16) + (av & 1) * 8;
+    }
+  }
+  // direct-load row/column of each of this lane's loads (K and V layouts differ)
+  int krow[Cfg::LOADS], kcb[Cfg::LOADS], vrow_[Cfg::LOADS], vcb[Cfg::LOADS];
+#pragma unroll
+  for (int j = 0; j < Cfg::LOADS; ++j) {
+    load_map<D, false>(j, wave, lane, krow[j], kcb[j]);
+    load_map<D, true>(j, wave, lane, vrow_[j], vcb[j]);
+  }
+
+  // ---- tile cursors over the flattened (range, 64-key tile) sequence
   const DevRange *rng = a.ranges + tile.r_begin;
   const int nr = tile.r_count;
-  int lr = 0;
-  while (lr < nr && rng[lr].begin >= rng[lr].end) ++lr;
-  int lk = lr < nr ? rng[lr].begin : 0;
-
-  // staging registers
-  uint4 kreg[Cfg::KCH];
-  uint2 vreg[8];
-  const int dq = tid % (D / 4), vcombo = tid / (D / 4);
-  const int vks = vcombo >> 1, vhh = vcombo & 1;
-
-  auto load_tile = [&](int r, int k0) {
-    const DevRange R = rng[r];
-    const Seg ks = a.k[R.seg], vs = a.v[R.seg];
-    const __bf16 *kb = (const __bf16 *)ks.p + b * ks.sb + h * ks.sh;
-    const __bf16 *vb = (const __bf16 *)vs.p + b * vs.sb + h * vs.sh;
-#pragma unroll
-    for (int i = 0; i < Cfg::KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      const int kidx = k0 + key;
-      if (kidx < R.end)
-        kreg[i] = *(const uint4 *)(kb + (int64_t)kidx * ks.sn + col * 8);
-      else
-        kreg[i] = uint4{0, 0, 0, 0};
-    }
-    if (tid < Cfg::VTASKS) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int key = vks * 16 + (s >> 2) * 8 + 4 * vhh + (s & 3);
-        const int kidx = k0 + key;
-        if (kidx < R.end)
-          vreg[s] = *(const uint2 *)(vb + (int64_t)kidx * vs.sn + dq * 4);
-        else
-          vreg[s] = uint2{0, 0};
-      }
-    }
+  auto first = [&](int &r, int &k) {
+    r = 0;
+    while (r < nr && rng[r].begin >= rng[r].end) ++r;
+    k = r < nr ? rng[r].begin : 0;
   };
-
-  auto store_tile = [&](int buf) {
-    char *Kl = smem + buf * BUF;
-    char *Vl = Kl + Cfg::KBYTES;
-#pragma unroll
-    for (int i = 0; i < Cfg::KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      *(uint4 *)(Kl + key * KSTR + col * 16) = kreg[i];
-    }
-    if (tid < Cfg::VTASKS) {
-      // V^T row d holds, at positions ks*16 + 8*hh + s, the keys ks*16 + (s/4)*8 + 4*hh + s%4:
-      // exactly the keys lane half hh holds in P^T slots s for key slice ks.
-      char *dst = Vl + (dq * 4) * VSTR + (vks * 16 + 8 * vhh) * 2;
-      uint4 o0, o1, o2, o3;
-      o0.x = pack_lo(vreg[0].x, vreg[1].x); o0.y = pack_lo(vreg[2].x, vreg[3].x);
-      o0.z = pack_lo(vreg[4].x, vreg[5].x); o0.w = pack_lo(vreg[6].x, vreg[7].x);
-      o1.x = pack_hi(vreg[0].x, vreg[1].x); o1.y = pack_hi(vreg[2].x, vreg[3].x);
-      o1.z = pack_hi(vreg[4].x, vreg[5].x); o1.w = pack_hi(vreg[6].x, vreg[7].x);
-      o2.x = pack_lo(vreg[0].y, vreg[1].y); o2.y = pack_lo(vreg[2].y, vreg[3].y);
-      o2.z = pack_lo(vreg[4].y, vreg[5].y); o2.w = pack_lo(vreg[6].y, vreg[7].y);
-      o3.x = pack_hi(vreg[0].y, vreg[1].y); o3.y = pack_hi(vreg[2].y, vreg[3].y);
-      o3.z = pack_hi(vreg[4].y, vreg[5].y); o3.w = pack_hi(vreg[6].y, vreg[7].y);
-      *(uint4 *)(dst + 0 * VSTR) = o0;
-      *(uint4 *)(dst + 1 * VSTR) = o1;
-      *(uint4 *)(dst + 2 * VSTR) = o2;
-      *(uint4 *)(dst + 3 * VSTR) = o3;
-    }
-  };
-
   auto advance = [&](int &r, int &k) {
+    if (r >= nr) return;
     k += BN;
     if (k >= rng[r].end) {
       ++r;
@@ -174,102 +166,184 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     }
   };
 
-  f32x16_t oacc[D / 32];
+  // Issue the direct loads of one tile (K or V of range r at key k) into LDS buffer `dst`.
+  auto issue = [&](int r, int k, bool is_v, int dst_off) {
+    const DevRange R = rng[r];
+    const Seg sg = is_v ? a.v[R.seg] : a.k[R.seg];
+    const char *base =
+        (const char *)sg.p + ((int64_t)b * sg.sb + (int64_t)h * sg.sh + (int64_t)k * sg.sn) * 2;
+    const int nvalid = min(BN, R.end - k);
+    const uint32_t sn2 = (uint32_t)sg.sn * 2u;
+    // all of this is uniform; readfirstlane keeps the descriptor in SGPRs
+    const uint64_t ub = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)ub);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(ub >> 32));
+    const int num = __builtin_amdgcn_readfirstlane((int)(nvalid * sn2));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(((uint64_t)hi << 32) | lo), (short)0, num, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
+    for (int j = 0; j < Cfg::LOADS; ++j) {
+      const uint32_t off = (uint32_t)(is_v ? vrow_[j] : krow[j]) * sn2 + (is_v ? vcb[j] : kcb[j]);
+      lds_char *dst = (lds_char *)smem + dst_off + (4 * j + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst,
+                                               16, (int)off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t oacc[Cfg::DB];
+#pragma unroll
+  for (int i = 0; i < Cfg::DB; ++i) oacc[i] = f32x16_t{};
   float m_run = -__builtin_inff();
   float l_part = 0.0f;
   const float c = a.c;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (lr < nr) {
-    load_tile(lr, lk);
-    store_tile(0);
+  // S^T = K . Q^T for the K tile in LDS buffer `kb_off`
+  auto qk_step = [&](const lds_char *Kl, int ds, f32x16_t &s0, f32x16_t &s1) {
+    const bf16x8_t a0 = *(const bf16x8_t *)(Kl + koff[ds]);
+    const bf16x8_t a1 = *(const bf16x8_t *)(Kl + 32 * ROWB + koff[ds]);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ds], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ds], s1, 0, 0, 0);
+  };
+
+  // Masks the scores of the tile at (r, k): s{kb}[i] is key k + kb*32 + (i/4)*8 + 4*hl + i%4 of
+  // this lane's query.  Only partial tiles and masked ranges come here.
+  auto apply_mask = [&](int r, int k, f32x16_t &s0, f32x16_t &s1) {
+    const DevRange R = rng[r];
+    if (R.mask == FA_MASK_NONE && k + BN <= R.end) return;
+    int klo = R.begin, khi = R.end;
+    if (R.mask == FA_MASK_SAME_FRAME) {
+      klo = max(klo, fq * T);
+      khi = min(khi, (fq + 1) * T);
+    } else if (R.mask == FA_MASK_GATE && fq < R.param) {
+      khi = klo;
+    }
+    const int base = k + 4 * hl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k0i = base + (i >> 2) * 8 + (i & 3);
+      const int k1i = k0i + 32;
+      if (k0i < klo || k0i >= khi) s0[i] = -__builtin_inff();
+      if (k1i < klo || k1i >= khi) s1[i] = -__builtin_inff();
+    }
+  };
+
+  // One pipeline step: softmax and PV of the tile whose scores are in (s0, s1) and whose V
+  // sits in LDS buffer `vbuf`, while S of the next tile (K in LDS buffer `kbuf`) accumulates in
+  // (n0, n1).  The MFMAs of the next S are independent of the softmax, and the scheduling
+  // hints interleave them with its VALU work.
+  auto step = [&](f32x16_t &s0, f32x16_t &s1, f32x16_t &n0, f32x16_t &n1, int kbuf, int vbuf) {
+    const lds_char *Kl = (const lds_char *)smem + kbuf * TILEB;
+    n0 = f32x16_t{};
+    n1 = f32x16_t{};
+    qk_step(Kl, 0, n0, n1);
+    qk_step(Kl, 1, n0, n1);
+    // row max of this tile (in-lane over 32 scores, then across the lane halves)
+    float mx = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s0[i]), s0[i + 1]);
+    mx = fmaxf(fmaxf(mx, s0[15]), s1[0]);
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), s1[i + 1]);
+    mx = fmaxf(mx, s1[15]);
+    qk_step(Kl, 2, n0, n1);
+    mx = xhalf_max(mx);
+    // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
+    const float mt = mx * c;
+    const bool need = mt > m_run + kThr;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+    m_run = need ? mt : m_run;
+    l_part *= alpha;
+    const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
+    u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      if ((i == 4 || i == 8 || i == 12) && 2 + i / 4 < Cfg::DS) qk_step(Kl, 2 + i / 4, n0, n1);
+      const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
+                           (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i + 1], c, mneg))};
+      const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg)),
+                           (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i + 1], c, mneg))};
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(e0, ones, l_part, false);
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(e1, ones, l_part, false);
+      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e0);
+      pw[2 + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e1);
+    }
+    if (Cfg::DS > 6) qk_step(Kl, 6, n0, n1);
+    if (Cfg::DS > 7) qk_step(Kl, 7, n0, n1);
+    // interleave: per MFMA of the next S, a slice of the softmax VALU
+#pragma unroll
+    for (int i = 0; i < 2 * Cfg::DS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
+    }
+    // O^T += V^T . P^T
+    const lds_char *Vl = (const lds_char *)smem + vbuf * TILEB;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < Cfg::DB; ++db) {
+        const lds_char *src = Vl + ks * 16 * ROWB + voff[db];
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t *)(src));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t *)(src + 8 * ROWB));
+        const s16x4_t both[2] = {lo, hi};
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            av, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Every wave waits for its own direct loads, then the barrier publishes all of them (and
+  // frees the buffers read in this step).
+  auto end_step = [&]() {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int cr = lr, ck = lk;
-    advance(lr, lk);
-    int buf = 0;
+  };
+
+  int cr, ck;  // tile j (softmax + PV)
+  first(cr, ck);
+  if (cr < nr) {
+    int vr = cr, vk = ck;  // tile j+1 (its V loads during step j)
+    advance(vr, vk);
+    int kr = vr, kk = vk;  // tile j+2 (its K loads during step j)
+    advance(kr, kk);
+    // prologue: K_0 -> buffer 0, V_0 -> buffer 2, K_1 -> buffer 1; S_0
+    issue(cr, ck, false, 0);
+    issue(cr, ck, true, 2 * TILEB);
+    if (vr < nr) issue(vr, vk, false, TILEB);
+    end_step();
+    f32x16_t sa0 = f32x16_t{}, sa1 = f32x16_t{}, sb0, sb1;
+    {
+      const lds_char *K0 = (const lds_char *)smem;
+#pragma unroll
+      for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(K0, ds, sa0, sa1);
+    }
+    // Steps alternate buffers: even steps read K buffer 1 / V buffer 2 and load K into buffer 0
+    // / V into buffer 3; odd steps the other way round.  Unrolled by two so the score registers
+    // swap roles instead of being copied.
     while (true) {
-      const bool has_next = lr < nr;
-      if (has_next) load_tile(lr, lk);
-
-      // ---- S^T = K . Q^T for 64 keys (two 32-key blocks)
-      const char *Kl = smem + buf * BUF;
-      const char *Vl = Kl + Cfg::KBYTES;
-      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        const bf16x8_t a0 = *(const bf16x8_t *)(Kl + l32 * KSTR + (ds * 16 + 8 * hl) * 2);
-        const bf16x8_t a1 = *(const bf16x8_t *)(Kl + (32 + l32) * KSTR + (ds * 16 + 8 * hl) * 2);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ds], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ds], s1, 0, 0, 0);
-      }
-
-      // ---- mask (partial tiles and masked ranges only).  s{kb}[r] is key
-      // ck + kb*32 + (r/4)*8 + 4*hl + r%4 for this lane's query.
-      const DevRange R = rng[cr];
-      if (R.mask != FA_MASK_NONE || ck + BN > R.end) {
-        int klo = R.begin, khi = R.end;
-        if (R.mask == FA_MASK_SAME_FRAME) {
-          klo = max(klo, fq * T);
-          khi = min(khi, (fq + 1) * T);
-        } else if (R.mask == FA_MASK_GATE && fq < R.param) {
-          khi = klo;
-        }
-        const int base = ck + 4 * hl;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int k0i = base + (r >> 2) * 8 + (r & 3);
-          const int k1i = k0i + 32;
-          if (k0i < klo || k0i >= khi) s0[r] = -__builtin_inff();
-          if (k1i < klo || k1i >= khi) s1[r] = -__builtin_inff();
-        }
-      }
-
-      // ---- online softmax (base 2, lazy rescale)
-      float mx = s0[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-      mx = xhalf_max(mx);
-      const float mt = mx * c;
-      const bool need = mt > m_run + kThr;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-        if (need) m_run = mt;
-        l_part *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      }
-      const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
-      bf16x8_t p[4];  // P^T operands for the four 16-key slices
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c, mneg));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], c, mneg));
-        l_part += e0 + e1;
-        p[r >> 3][r & 7] = (__bf16)e0;
-        p[2 + (r >> 3)][r & 7] = (__bf16)e1;
-      }
-
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8_t av =
-              *(const bf16x8_t *)(Vl + (db * 32 + l32) * VSTR + (ks * 16 + 8 * hl) * 2);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[ks], oacc[db], 0, 0, 0);
-        }
-      }
-
-      if (has_next) store_tile(buf ^ 1);
-      __syncthreads();
-      if (!has_next) break;
-      cr = lr;
-      ck = lk;
-      advance(lr, lk);
-      buf ^= 1;
+      // even step j: S_j in (sa), next S into (sb)
+      apply_mask(cr, ck, sa0, sa1);
+      if (kr < nr) issue(kr, kk, false, 0);
+      if (vr < nr) issue(vr, vk, true, 3 * TILEB);
+      step(sa0, sa1, sb0, sb1, 1, 2);
+      end_step();
+      if (vr >= nr) break;
+      cr = vr; ck = vk; vr = kr; vk = kk; advance(kr, kk);
+      // odd step
+      apply_mask(cr, ck, sb0, sb1);
+      if (kr < nr) issue(kr, kk, false, TILEB);
+      if (vr < nr) issue(vr, vk, true, 2 * TILEB);
+      step(sb0, sb1, sa0, sa1, 0, 3);
+      end_step();
+      if (vr >= nr) break;
+      cr = vr; ck = vk; vr = kr; vk = kk; advance(kr, kk);
     }
   }
 
@@ -280,7 +354,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   const Seg os = a.o[tile.q_kind];
   __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < Cfg::DB; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
