@@ -44,6 +44,26 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
+// The block map is read-only for the kernel's lifetime: reading it through the constant
+// address space turns its loads into scalar (SMEM) loads.  Vector loads would share the
+// in-order VMEM counter with the tile prefetches, and every wait on them would also wait
+// for the prefetch in flight.
+typedef __attribute__((address_space(4))) const DevRange cRange;
+typedef __attribute__((address_space(4))) const DevTile cTile;
+typedef __attribute__((address_space(4))) const DevWork cWork;
+
+// Copies a block-map record out of the constant address space, word by word.
+template <typename T, typename CT>
+__device__ __forceinline__ T cload(const CT *p) {
+  static_assert(sizeof(T) % 4 == 0, "block-map records are whole words");
+  typedef __attribute__((address_space(4))) const int cint;
+  const cint *q = (const cint *)p;
+  T v;
+  int *d = (int *)&v;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) d[i] = q[i];
+  return v;
+}
 
 // Raw buffer descriptor word 3 for gfx9-family loads (32-bit data, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
@@ -69,11 +89,12 @@ struct Bf16Cfg {
   static constexpr int LOADS = TILEB / (256 * 16);  // 16-byte direct loads per thread per tile
   static constexpr int DS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;             // 32-channel blocks of O^T
-  // K: chunk c of row r lives at chunk c ^ (r % CH); V: at c ^ ((2r) % CH).  Both keep the
-  // MFMA operand reads (ds_read_b128 over 16 rows; ds_read_b64_tr_b16 over 4 rows x 2 chunks)
-  // on distinct banks.
+  // K: chunk c of row r lives at chunk c ^ (r % CH): a ds_read_b128 of 16 lanes (16 rows, one
+  // logical chunk) hits 16 distinct chunk slots.  V: at c ^ ((4r) % CH): a transposing read of
+  // a half wave (4 rows x 4 logical chunks x 2 halves, rows differing in their low 2 bits)
+  // again hits 16 distinct slots (with D = 64 two rows share a slot).
   __device__ static int ksw(int r) { return r & (CH - 1); }
-  __device__ static int vsw(int r) { return (2 * r) & (CH - 1); }
+  __device__ static int vsw(int r) { return (4 * r) & (CH - 1); }
 };
 
 // Where each lane's direct loads of a tile land and which bytes of the tile's
@@ -94,12 +115,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   using Cfg = Bf16Cfg<D>;
   constexpr int BN = Cfg::BN, ROWB = Cfg::ROWB, TILEB = Cfg::TILEB;
   constexpr float kThr = 8.0f;
-  // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  // LDS: two K and two V tile buffers.  Separate arrays (not one array indexed by buffer) let
+  // the compiler see that direct loads into one buffer never alias reads of another, so it
+  // does not wait for in-flight prefetches before every LDS read.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
 
-  const DevWork w = a.work[blockIdx.x];
+  const DevWork w = cload<DevWork>((const cWork *)a.work + blockIdx.x);
   if (w.tile < 0) return;
-  const DevTile tile = a.tiles[w.tile];
+  const DevTile tile = cload<DevTile>((const cTile *)a.tiles + w.tile);
   const int b = w.bh / a.H, h = w.bh - (w.bh / a.H) * a.H;
   const int tid = threadIdx.x;
   // the wave index is uniform per wave; say so, since it feeds M0 (LDS address of direct loads)
@@ -148,46 +174,64 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     load_map<D, true>(j, wave, lane, vrow_[j], vcb[j]);
   }
 
-  // ---- tile cursors over the flattened (range, 64-key tile) sequence
-  const DevRange *rng = a.ranges + tile.r_begin;
+  // ---- tile cursors over the flattened (range, 64-key tile) sequence.  Each cursor keeps the
+  // fields of its current range (and, for the load cursors, the (batch, head) base of the
+  // range's tensor) in scalar registers; the block map is only read again when a cursor
+  // crosses into the next range, a few times per work item.
+  const cRange *rng = (const cRange *)a.ranges + tile.r_begin;
   const int nr = tile.r_count;
-  auto first = [&](int &r, int &k) {
-    r = 0;
-    while (r < nr && rng[r].begin >= rng[r].end) ++r;
-    k = r < nr ? rng[r].begin : 0;
+  struct Cur {
+    int r, k, begin, end, mask, param;
+    uint64_t base;  // byte address of (b, key 0, h) of the range's K or V tensor
+    uint32_t sn2;   // bytes between consecutive keys
   };
-  auto advance = [&](int &r, int &k) {
+  // kind: 0 = no tensor (mask cursor), 1 = K, 2 = V
+  auto enter = [&](Cur &c, int r, int kind) {
+    while (r < nr && rng[r].begin >= rng[r].end) ++r;
+    c.r = r;
     if (r >= nr) return;
-    k += BN;
-    if (k >= rng[r].end) {
-      ++r;
-      while (r < nr && rng[r].begin >= rng[r].end) ++r;
-      k = r < nr ? rng[r].begin : 0;
+    const DevRange R = cload<DevRange>(rng + r);
+    c.k = c.begin = R.begin;
+    c.end = R.end;
+    c.mask = R.mask;
+    c.param = R.param;
+    if (kind) {
+      const Seg sg = kind == 2 ? a.v[R.seg] : a.k[R.seg];
+      c.base = (uint64_t)sg.p + (uint64_t)((int64_t)b * sg.sb + (int64_t)h * sg.sh) * 2u;
+      c.sn2 = (uint32_t)sg.sn * 2u;
     }
+  };
+  auto next = [&](Cur &c, int kind) {
+    if (c.r >= nr) return;
+    c.k += BN;
+    if (c.k >= c.end) enter(c, c.r + 1, kind);
   };
 
-  // Issue the direct loads of one tile (K or V of range r at key k) into LDS buffer `dst`.
-  auto issue = [&](int r, int k, bool is_v, int dst_off) {
-    const DevRange R = rng[r];
-    const Seg sg = is_v ? a.v[R.seg] : a.k[R.seg];
-    const char *base =
-        (const char *)sg.p + ((int64_t)b * sg.sb + (int64_t)h * sg.sh + (int64_t)k * sg.sn) * 2;
-    const int nvalid = min(BN, R.end - k);
-    const uint32_t sn2 = (uint32_t)sg.sn * 2u;
-    // all of this is uniform; readfirstlane keeps the descriptor in SGPRs
-    const uint64_t ub = (uint64_t)base;
+  // Buffer descriptor of the tile at cursor c (K or V).  It covers only the keys of the range,
+  // so the hardware returns zeros past its end; a cursor past the last range gets an empty
+  // descriptor (its loads return zeros into a buffer nobody reads).
+  auto tile_rsrc = [&](const Cur &c) {
+    const bool live = c.r < nr;
+    const uint64_t ub = c.base + (uint64_t)(uint32_t)c.k * c.sn2;
+    const int nvalid = live ? min(BN, c.end - c.k) : 0;
+    // all uniform; readfirstlane keeps the descriptor in SGPRs
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)ub);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(ub >> 32));
-    const int num = __builtin_amdgcn_readfirstlane((int)(nvalid * sn2));
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(((uint64_t)hi << 32) | lo), (short)0, num, kBufferFlags);
+    const int num = __builtin_amdgcn_readfirstlane((int)(nvalid * c.sn2));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, num,
+                                             kBufferFlags);
+  };
+  // Direct load j of this lane's share of a K (is_v = false) or V tile into LDS buffer `buf`.
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t sn2, bool is_v, char *buf, int j) {
+    const uint32_t off = (uint32_t)(is_v ? vrow_[j] : krow[j]) * sn2 + (is_v ? vcb[j] : kcb[j]);
+    lds_char *dst = (lds_char *)buf + (4 * j + wave) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
+                                             (int)off, 0, 0, 0);
+  };
+  auto issue = [&](const Cur &c, bool is_v, char *buf) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c);
 #pragma unroll
-    for (int j = 0; j < Cfg::LOADS; ++j) {
-      const uint32_t off = (uint32_t)(is_v ? vrow_[j] : krow[j]) * sn2 + (is_v ? vcb[j] : kcb[j]);
-      lds_char *dst = (lds_char *)smem + dst_off + (4 * j + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst,
-                                               16, (int)off, 0, 0, 0);
-    }
+    for (int j = 0; j < Cfg::LOADS; ++j) load_one(rs, c.sn2, is_v, buf, j);
   };
 
   f32x16_t oacc[Cfg::DB];
@@ -206,19 +250,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ds], s1, 0, 0, 0);
   };
 
-  // Masks the scores of the tile at (r, k): s{kb}[i] is key k + kb*32 + (i/4)*8 + 4*hl + i%4 of
-  // this lane's query.  Only partial tiles and masked ranges come here.
-  auto apply_mask = [&](int r, int k, f32x16_t &s0, f32x16_t &s1) {
-    const DevRange R = rng[r];
-    if (R.mask == FA_MASK_NONE && k + BN <= R.end) return;
-    int klo = R.begin, khi = R.end;
-    if (R.mask == FA_MASK_SAME_FRAME) {
+  // Masks the scores of the tile at cursor c: s{kb}[i] is key c.k + kb*32 + (i/4)*8 + 4*hl + i%4
+  // of this lane's query.  Only partial tiles and masked ranges come here.
+  auto apply_mask = [&](const Cur &c, f32x16_t &s0, f32x16_t &s1) {
+    if (c.mask == FA_MASK_NONE && c.k + BN <= c.end) return;
+    int klo = c.begin, khi = c.end;
+    if (c.mask == FA_MASK_SAME_FRAME) {
       klo = max(klo, fq * T);
       khi = min(khi, (fq + 1) * T);
-    } else if (R.mask == FA_MASK_GATE && fq < R.param) {
+    } else if (c.mask == FA_MASK_GATE && fq < c.param) {
       khi = klo;
     }
-    const int base = k + 4 * hl;
+    const int base = c.k + 4 * hl;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int k0i = base + (i >> 2) * 8 + (i & 3);
@@ -232,12 +275,27 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   // sits in LDS buffer `vbuf`, while S of the next tile (K in LDS buffer `kbuf`) accumulates in
   // (n0, n1).  The MFMAs of the next S are independent of the softmax, and the scheduling
   // hints interleave them with its VALU work.
-  auto step = [&](f32x16_t &s0, f32x16_t &s1, f32x16_t &n0, f32x16_t &n1, int kbuf, int vbuf) {
-    const lds_char *Kl = (const lds_char *)smem + kbuf * TILEB;
+  auto step = [&](f32x16_t &s0, f32x16_t &s1, f32x16_t &n0, f32x16_t &n1, const char *kbuf,
+                  const char *vbuf, const Cur &kc, char *kdst, const Cur &vc, char *vdst) {
+    const lds_char *Kl = (const lds_char *)kbuf;
+    // prefetch of K (two tiles ahead) and V (one tile ahead), one direct load per k-step of the
+    // next S so the loads trickle into the memory pipeline instead of arriving in one burst
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
+    auto prefetch = [&](int ds) {
+#pragma unroll
+      for (int li = ds * 2 * Cfg::LOADS / Cfg::DS; li < (ds + 1) * 2 * Cfg::LOADS / Cfg::DS; ++li) {
+        if (li < Cfg::LOADS)
+          load_one(krs, kc.sn2, false, kdst, li);
+        else
+          load_one(vrs, vc.sn2, true, vdst, li - Cfg::LOADS);
+      }
+    };
     n0 = f32x16_t{};
     n1 = f32x16_t{};
     qk_step(Kl, 0, n0, n1);
+    prefetch(0);
     qk_step(Kl, 1, n0, n1);
+    prefetch(1);
     // row max of this tile (in-lane over 32 scores, then across the lane halves)
     float mx = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
 #pragma unroll
@@ -247,6 +305,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), s1[i + 1]);
     mx = fmaxf(mx, s1[15]);
     qk_step(Kl, 2, n0, n1);
+    prefetch(2);
     mx = xhalf_max(mx);
     // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
     const float mt = mx * c;
@@ -258,7 +317,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      if ((i == 4 || i == 8 || i == 12) && 2 + i / 4 < Cfg::DS) qk_step(Kl, 2 + i / 4, n0, n1);
+      if ((i == 4 || i == 8 || i == 12) && 2 + i / 4 < Cfg::DS) {
+        qk_step(Kl, 2 + i / 4, n0, n1);
+        prefetch(2 + i / 4);
+      }
       const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
                            (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i + 1], c, mneg))};
       const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg)),
@@ -268,12 +330,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
       pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e0);
       pw[2 + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e1);
     }
-    if (Cfg::DS > 6) qk_step(Kl, 6, n0, n1);
-    if (Cfg::DS > 7) qk_step(Kl, 7, n0, n1);
-    // interleave: per MFMA of the next S, a slice of the softmax VALU
+    if (Cfg::DS > 6) {
+      qk_step(Kl, 6, n0, n1);
+      prefetch(6);
+    }
+    if (Cfg::DS > 7) {
+      qk_step(Kl, 7, n0, n1);
+      prefetch(7);
+    }
+    // interleave: per MFMA of the next S, a slice of the softmax VALU, and a direct load every
+    // other MFMA
 #pragma unroll
     for (int i = 0; i < 2 * Cfg::DS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
     }
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -281,7 +351,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
       for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
     }
     // O^T += V^T . P^T
-    const lds_char *Vl = (const lds_char *)smem + vbuf * TILEB;
+    const lds_char *Vl = (const lds_char *)vbuf;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -306,44 +376,44 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     __syncthreads();
   };
 
-  int cr, ck;  // tile j (softmax + PV)
-  first(cr, ck);
-  if (cr < nr) {
-    int vr = cr, vk = ck;  // tile j+1 (its V loads during step j)
-    advance(vr, vk);
-    int kr = vr, kk = vk;  // tile j+2 (its K loads during step j)
-    advance(kr, kk);
-    // prologue: K_0 -> buffer 0, V_0 -> buffer 2, K_1 -> buffer 1; S_0
-    issue(cr, ck, false, 0);
-    issue(cr, ck, true, 2 * TILEB);
-    if (vr < nr) issue(vr, vk, false, TILEB);
+  Cur cc, cv, ck;  // tile j (mask, softmax, PV); tile j+1 (V loads); tile j+2 (K loads)
+  enter(cc, 0, 0);
+  if (cc.r < nr) {
+    enter(cv, cc.r, 2);
+    Cur k0c, k1c;  // prologue K tiles 0 and 1
+    enter(k0c, cc.r, 1);
+    k1c = k0c;
+    next(k1c, 1);
+    // prologue: K_0 -> kbuf0, V_0 -> vbuf0, K_1 -> kbuf1; S_0
+    issue(k0c, false, kbuf0);
+    issue(cv, true, vbuf0);
+    if (k1c.r < nr) issue(k1c, false, kbuf1);
+    next(cv, 2);       // now tile 1
+    ck = k1c;
+    next(ck, 1);       // now tile 2
     end_step();
     f32x16_t sa0 = f32x16_t{}, sa1 = f32x16_t{}, sb0, sb1;
     {
-      const lds_char *K0 = (const lds_char *)smem;
+      const lds_char *K0 = (const lds_char *)kbuf0;
 #pragma unroll
       for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(K0, ds, sa0, sa1);
     }
-    // Steps alternate buffers: even steps read K buffer 1 / V buffer 2 and load K into buffer 0
-    // / V into buffer 3; odd steps the other way round.  Unrolled by two so the score registers
-    // swap roles instead of being copied.
+    // Steps alternate buffers: even steps read kbuf1 / vbuf0 and load K into kbuf0 / V into
+    // vbuf1; odd steps the other way round.  Unrolled by two so the score registers swap roles
+    // instead of being copied.
     while (true) {
       // even step j: S_j in (sa), next S into (sb)
-      apply_mask(cr, ck, sa0, sa1);
-      if (kr < nr) issue(kr, kk, false, 0);
-      if (vr < nr) issue(vr, vk, true, 3 * TILEB);
-      step(sa0, sa1, sb0, sb1, 1, 2);
+      apply_mask(cc, sa0, sa1);
+      step(sa0, sa1, sb0, sb1, kbuf1, vbuf0, ck, kbuf0, cv, vbuf1);
       end_step();
-      if (vr >= nr) break;
-      cr = vr; ck = vk; vr = kr; vk = kk; advance(kr, kk);
+      if (cv.r >= nr) break;
+      next(cc, 0); next(cv, 2); next(ck, 1);
       // odd step
-      apply_mask(cr, ck, sb0, sb1);
-      if (kr < nr) issue(kr, kk, false, TILEB);
-      if (vr < nr) issue(vr, vk, true, 2 * TILEB);
-      step(sb0, sb1, sa0, sa1, 0, 3);
+      apply_mask(cc, sb0, sb1);
+      step(sb0, sb1, sa0, sa1, kbuf0, vbuf1, ck, kbuf1, cv, vbuf0);
       end_step();
-      if (vr >= nr) break;
-      cr = vr; ck = vk; vr = kr; vk = kk; advance(kr, kk);
+      if (cv.r >= nr) break;
+      next(cc, 0); next(cv, 2); next(ck, 1);
     }
   }
 
