@@ -226,6 +226,81 @@ def cpu_baseline(W, budget_s):
                       "keys each) of the 1560-token 40-head stream, %.1f s" % (done_rows, keys, spent)}
 
 
+def summarize_rocprof(prefix, out_dir):
+    """Writes the committed rocprofv3 summaries from the CSV output of the commands below
+    (run with this same bench.py): kernel trace statistics, and HBM traffic of the attention
+    kernel per launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the counter reads for the
+    plain 1 GiB device copy that --copy-check runs in the same process."""
+    import csv
+    import glob
+    import fa_workloads as W
+    from frame_aligned_attention_amd import binding as B
+    cmd = "python bench.py --steps 20 --warmup 20 --no-cpu-baseline --no-extra --copy-check 1024"
+    trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d %s_trace -o trace -- %s"
+                 % (prefix, cmd))
+    stats = list(csv.DictReader(open(glob.glob(prefix + "_trace/*kernel_stats.csv")[0])))
+    lines = ["# rocprofv3 kernel statistics: 1560-token 40-head stream, 20 warm-up + 20 timed "
+             "chunks (attention + ring append each), after a 1 GiB calibration copy",
+             "# command: " + trace_cmd,
+             "# kernel source sha256[:16] (fa_attn_bf16.hip): " + kernel_sha(),
+             "%-44s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for r in stats[:8]:
+        name = r["Name"]
+        name = name if len(name) <= 44 else name[:41] + "..."
+        lines.append("%-44s %6s %12.1f %12.1f %12.1f" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3))
+    os.makedirs(out_dir, exist_ok=True)
+    open(os.path.join(out_dir, "attn_bf16_stream1560_h40_trace.txt"), "w").write(
+        "\n".join(lines) + "\n")
+
+    def per_dispatch(counter):
+        rows = list(csv.DictReader(open(glob.glob(prefix + "_%s/*counter_collection.csv"
+                                                  % counter)[0])))
+        d = {}
+        for r in rows:
+            k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            d[k] = d.get(k, 0.0) + float(r["Counter_Value"])
+        return sorted(d.items())
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        items = per_dispatch(counter)
+        copy = max(v for (i, n), v in items if "copyBuffer" in n or "copy" in n.lower())
+        factor = (1 << 30) / (copy * 1024.0)
+        attn = [v for (i, n), v in items if "attn_bf16" in n]
+        timed = attn[20:40]  # 20 warm-up launches, then the 20 timed ones
+        res[counter] = (factor, sum(timed) / len(timed) * 1024.0 * factor, copy)
+    w = W.WORKLOADS[2]
+    d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=0,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=B.FA_Q_TARGET)
+    s = B.Stream(d)
+    alg = []
+    for ch in range(w.chunks):
+        s.seek(ch * w.C, max(0, ch * w.C - w.cache_frames))
+        alg.append(B.fa_layout_stats(s.layout())["bytes"])
+    alg_mean = sum(alg) / len(alg)
+    hbm = res["FETCH_SIZE"][1] + res["WRITE_SIZE"][1]
+    text = [
+        "# HBM traffic of attn_bf16_kernel<128>, per launch, mean over the 20 timed chunks of the",
+        "# 1560-token 40-head stream (chunks 0..19: warm-up and steady state)",
+        "# commands (one rocprofv3 pass per counter):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s_FETCH_SIZE -o pmc -- %s" % (prefix, cmd),
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s_WRITE_SIZE -o pmc -- %s" % (prefix, cmd),
+        "# calibration: the same runs first copy 1 GiB device to device (--copy-check 1024);",
+        "#   FETCH_SIZE read %.0f KiB for it -> scale %.4f; WRITE_SIZE read %.0f KiB -> scale %.4f"
+        % (res["FETCH_SIZE"][2], res["FETCH_SIZE"][0], res["WRITE_SIZE"][2], res["WRITE_SIZE"][0]),
+        "kernel_source_sha256_16: %s" % kernel_sha(),
+        "fetch_bytes_per_launch: %.4e" % res["FETCH_SIZE"][1],
+        "write_bytes_per_launch: %.4e" % res["WRITE_SIZE"][1],
+        "hbm_bytes_per_launch: %.4e" % hbm,
+        "algorithmic_bytes_per_launch: %.4e" % alg_mean,
+        "traffic_over_algorithmic: %.3f" % (hbm / alg_mean),
+    ]
+    open(os.path.join(out_dir, "attn_bf16_stream1560_h40_traffic.txt"), "w").write(
+        "\n".join(text) + "\n")
+    print("\n".join(lines + text))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,9 +309,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other bf16 workloads")
+    ap.add_argument("--summarize-rocprof", metavar="PREFIX",
+                    help="write profiles/ summaries from rocprofv3 CSVs under PREFIX_{trace,"
+                         "FETCH_SIZE,WRITE_SIZE} and exit")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (calibrates HBM counters)")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the attention "
               "shards by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
