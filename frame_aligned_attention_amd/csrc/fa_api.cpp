@@ -166,9 +166,99 @@ static fa_status ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
   return FA_OK;
 }
 
+static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out,
+                                 int32_t flags, hipStream_t stream) {
+  if (!L || !in || !out) return fail(FA_ERR_INVALID, "NULL argument");
+  const fa_layout_desc &d = L->d;
+  if (d.dtype != FA_LOWBIT) return fail(FA_ERR_INVALID, "layout is not FA_LOWBIT");
+  if (flags & ~FA_QUANT_MEAN_GIVEN) return fail(FA_ERR_INVALID, "unknown flags");
+  if (!out->k_mean || !out->v_absmax) return fail(FA_ERR_INVALID, "k_mean / v_absmax is NULL");
+  const int T = d.tokens_per_frame;
+  QuantArgs qa{};
+  qa.H = d.heads;
+  qa.D = d.head_dim;
+  qa.batch = d.batch;
+  qa.k_mean = out->k_mean;
+  qa.v_absmax = out->v_absmax;
+  qa.softmax_scale = d.scale;
+  int nseg = 0, blocks = 0;
+  auto add = [&](const fa_tensor &ti, const fa_tensor &to, int ntok, int kind, int lo0, int hi0,
+                 int lo1, int hi1, const char *name) -> fa_status {
+    fa_status st = check_tensor(ti, 2, d.batch, name, false);
+    if (st != FA_OK) return st;
+    st = check_tensor(to, 1, d.batch, name, true);
+    if (st != FA_OK) return st;
+    if (nseg >= kMaxQSeg) return fail(FA_ERR_UNSUPPORTED, "too many tensors to quantise");
+    QSeg &g = qa.seg[nseg++];
+    g.in = ti.data; g.isb = ti.stride_b; g.isn = ti.stride_n; g.ish = ti.stride_h;
+    g.out = to.data; g.osb = to.stride_b; g.osn = to.stride_n; g.osh = to.stride_h;
+    g.scale = to.scale;
+    g.nblk = (ntok + kQuantBlock - 1) / kQuantBlock;
+    g.kind = kind;
+    g.lo0 = lo0; g.hi0 = hi0; g.lo1 = lo1; g.hi1 = hi1;
+    g.blk_begin = blocks;
+    g.n = ntok;
+    g.lse = nullptr;
+    blocks += g.nblk;
+    return FA_OK;
+  };
+  const fa_tensor *qi[3] = {&in->q_tgt, &in->q_src, &in->q_ref};
+  const fa_tensor *qo[3] = {&out->q_tgt, &out->q_src, &out->q_ref};
+  fa_status st;
+  for (int k = 0; k < 3; ++k) {
+    if (!L->q_rows[k]) continue;
+    st = add(*qi[k], *qo[k], L->q_rows[k], 0, 0, L->q_rows[k], 0, 0, kQName[k]);
+    if (st != FA_OK) return st;
+    qa.seg[nseg - 1].lse = k == 0 ? out->lse_tgt : k == 1 ? out->lse_src : out->lse_ref;
+  }
+  // key tensors the block map reads, and the ring's slot runs in view
+  bool used[4] = {false, false, false, false};
+  int rlo[2] = {0, 0}, rhi[2] = {0, 0}, nrun = 0;
+  for (const DevRange &r : L->ranges) {
+    used[r.seg] = true;
+    if (r.seg == FA_SEG_RING) {
+      bool seen = false;
+      for (int i = 0; i < nrun; ++i) seen |= (rlo[i] == r.begin && rhi[i] == r.end);
+      if (!seen) {
+        if (nrun >= 2) return fail(FA_ERR_UNSUPPORTED, "more than two ring runs");
+        rlo[nrun] = r.begin;
+        rhi[nrun] = r.end;
+        ++nrun;
+      }
+    }
+  }
+  const fa_tensor *ki[4] = {&in->k_ring, &in->k_tgt, &in->k_src, &in->k_ref};
+  const fa_tensor *ko[4] = {&out->k_ring, &out->k_tgt, &out->k_src, &out->k_ref};
+  const fa_tensor *vi[4] = {&in->v_ring, &in->v_tgt, &in->v_src, &in->v_ref};
+  const fa_tensor *vo[4] = {&out->v_ring, &out->v_tgt, &out->v_src, &out->v_ref};
+  const int seg_tok[4] = {d.cache_frames * T, d.frames * T, d.frames * T, L->ref_total};
+  for (int kind = 1; kind <= 2; ++kind)
+    for (int sgi = 0; sgi < 4; ++sgi) {
+      if (!used[sgi]) continue;
+      const int n = seg_tok[sgi];
+      const int lo0 = sgi == FA_SEG_RING ? rlo[0] : 0, hi0 = sgi == FA_SEG_RING ? rhi[0] : n;
+      const int lo1 = sgi == FA_SEG_RING ? rlo[1] : 0, hi1 = sgi == FA_SEG_RING ? rhi[1] : 0;
+      st = add(kind == 1 ? *ki[sgi] : *vi[sgi], kind == 1 ? *ko[sgi] : *vo[sgi], n, kind, lo0,
+               hi0, lo1, hi1, kind == 1 ? kKName[sgi] : kVName[sgi]);
+      if (st != FA_OK) return st;
+    }
+  qa.nseg = nseg;
+  qa.total_blocks = blocks;
+  if ((int64_t)blocks * d.batch * d.heads >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "too many quantisation blocks");
+  hipError_t e = launch_quant_lowbit(qa, (flags & FA_QUANT_MEAN_GIVEN) != 0, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("quantiser launch: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace fa
 
 using namespace fa;
+
+extern "C" fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out,
+                                        int32_t flags, fa_hip_stream stream) {
+  return quantize_lowbit(L, in, out, flags, (hipStream_t)stream);
+}
 
 extern "C" const char *fa_status_str(fa_status s) {
   switch (s) {

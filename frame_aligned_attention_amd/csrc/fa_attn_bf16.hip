@@ -34,7 +34,7 @@
 // exceeds it by more than 8 (so p <= 2^8): the O/l rescale is then rare.
 // Row sums are taken on the bf16-rounded p that feed the PV product
 // (v_dot2c_f32_bf16 against ones).
-#include "fa_internal.h"
+#include "fa_device.h"
 
 namespace fa {
 
@@ -43,43 +43,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-// The block map is read-only for the kernel's lifetime: reading it through the constant
-// address space turns its loads into scalar (SMEM) loads.  Vector loads would share the
-// in-order VMEM counter with the tile prefetches, and every wait on them would also wait
-// for the prefetch in flight.
-typedef __attribute__((address_space(4))) const DevRange cRange;
-typedef __attribute__((address_space(4))) const DevTile cTile;
-typedef __attribute__((address_space(4))) const DevWork cWork;
-
-// Copies a block-map record out of the constant address space, word by word.
-template <typename T, typename CT>
-__device__ __forceinline__ T cload(const CT *p) {
-  static_assert(sizeof(T) % 4 == 0, "block-map records are whole words");
-  typedef __attribute__((address_space(4))) const int cint;
-  const cint *q = (const cint *)p;
-  T v;
-  int *d = (int *)&v;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) d[i] = q[i];
-  return v;
-}
-
-// Raw buffer descriptor word 3 for gfx9-family loads (32-bit data, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ float xhalf_max(float x) {
-  // v_permlane32_swap with both operands = x leaves, in every lane, the pair
-  // (x of lane l%32, x of lane 32 + l%32).
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float xhalf_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 template <int D>
 struct Bf16Cfg {
   static constexpr int BN = kBf16BlockN;        // keys per tile
@@ -214,12 +177,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     const bool live = c.r < nr;
     const uint64_t ub = c.base + (uint64_t)(uint32_t)c.k * c.sn2;
     const int nvalid = live ? min(BN, c.end - c.k) : 0;
-    // all uniform; readfirstlane keeps the descriptor in SGPRs
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)ub);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(ub >> 32));
-    const int num = __builtin_amdgcn_readfirstlane((int)(nvalid * c.sn2));
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, num,
-                                             kBufferFlags);
+    return make_rsrc(ub, (int)(nvalid * c.sn2));
   };
   // Direct load j of this lane's share of a K (is_v = false) or V tile into LDS buffer `buf`.
   auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t sn2, bool is_v, char *buf, int j) {

@@ -87,28 +87,35 @@ hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, int grid, hipStream_
 hipError_t launch_attn_lowbit(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);
 
-struct QuantSeg {
-  const void *in;         // bf16
-  int64_t isb, isn, ish;
-  void *out;              // int8 or e4m3 codes
-  int64_t osb, osn, osh;
-  float *scale;           // [b][h][nblk]
+// One tensor for the low-bit quantiser: bf16 input, 1-byte codes out (same token-major layout),
+// fp32 scales per (batch, head, 128-token block).  Only tokens in up to two runs
+// [lo0, hi0), [lo1, hi1) are read and written (ring frames outside the call's view are not).
+struct QSeg {
+  const void *in;
+  int64_t isb, isn, ish;  // elements
+  void *out;
+  int64_t osb, osn, osh;  // elements (bytes)
+  float *scale;           // [batch][heads][nblk]
+  int32_t nblk;
+  int32_t kind;           // 0: Q int8, 1: K int8 after the mean, 2: V e4m3
+  int32_t lo0, hi0, lo1, hi1;
+  int32_t blk_begin;      // first entry of this tensor in the flat block list
   int32_t n;              // tokens
-  int32_t kind;           // 0: Q (int8), 1: K (int8, mean-subtracted), 2: V (e4m3)
-  // ring segments: only tokens of frames in view are quantised
-  int32_t ring_lo_tok, ring_hi_tok;   // token range [lo, hi) in view; or whole segment
-  int32_t ring_lo2_tok, ring_hi2_tok; // second run (wrap); empty if lo2 >= hi2
+  float *lse;             // Q tensors: per-row smoothing shift scale*q.m -> [batch][heads][n]
 };
+
+constexpr int kMaxQSeg = 12;
 
 struct QuantArgs {
-  QuantSeg seg[11];
+  QSeg seg[kMaxQSeg];
   int32_t nseg;
+  int32_t total_blocks;   // sum of nblk
   int32_t H, D, batch;
-  float *k_mean;          // [b][h][D]
-  float *v_absmax;        // [b][h]
-  int32_t mean_given;
+  float *k_mean;          // [batch][heads][D]
+  float *v_absmax;        // [batch][heads]: largest V block scale, written with atomic max
+  float softmax_scale;
 };
 
-hipError_t launch_quant_lowbit(const QuantArgs &a, hipStream_t s);
+hipError_t launch_quant_lowbit(const QuantArgs &a, bool mean_given, hipStream_t s);
 
 }  // namespace fa

@@ -1,17 +1,479 @@
-// fa_lowbit.hip -- low-bit path (int8 Q.K^T, fp8 e4m3 P.V) and its quantiser.
-#include "fa_internal.h"
+// fa_lowbit.hip -- the low-bit frame-aligned attention path for gfx950: the
+// quantiser (per-head key mean, per-128-token-block int8 Q/K and e4m3 V) and the
+// attention kernel with int8 Q.K^T (v_mfma_i32_32x32x32_i8) and e4m3 P.V
+// (v_mfma_scale_f32_32x32x64_f8f6f4), fp32 online softmax.
+//
+// The pages name low-bit attention only ("Vidu S2" launch article, technical
+// stack section; tech report, hybrid-attention paragraph).  What it computes here:
+//  - K is reduced by one per-(batch, head) channel mean m of the call's keys;
+//    the softmax does not change (q.m is constant along a row);
+//  - Q and K: symmetric int8 per (batch, head, 128-token block), scale
+//    absmax/127, code = round_half_even(x * (127/absmax));
+//  - V: OCP e4m3 per block, scale absmax/448 (v_cvt_pk_fp8_f32 rounds to
+//    nearest even);
+//  - scores s = (q8 . k8) * sq * sk * softmax_scale, exact running max,
+//    p = 2^(s*log2e - m) in fp32, row sums l of p in fp32;
+//  - P.V in e4m3: p' = p * 448 * sv / U with U the largest V block scale of the
+//    call, so p' <= 448; O = (U / 448) * sum(p' v8) / l.
+// Key tiles never straddle a 128-token block (a range's first tile ends at the
+// next 64-key boundary), so K and V scales are uniform per tile.
+#include "fa_device.h"
 
 namespace fa {
 
-hipError_t launch_attn_lowbit(const AttnArgs &, int, int, hipStream_t) {
-  return hipErrorNotSupported;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// ============================================================== quantiser
+
+__global__ void __launch_bounds__(64) quant_init_kernel(float *v_absmax, int n) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i < n) v_absmax[i] = 0.0f;
 }
 
-hipError_t launch_quant_lowbit(const QuantArgs &, hipStream_t) { return hipErrorNotSupported; }
+// Per-(batch, head) channel mean of the keys in view.  One workgroup per (b, h, 8 channels):
+// 256 token lanes each sum a strided share in fp32, then a fixed-order tree: deterministic.
+__global__ void __launch_bounds__(256) kmean_kernel(const QuantArgs a) {
+  const int nchunk = a.D / 8;
+  const int bh = blockIdx.x / nchunk, ch = (blockIdx.x % nchunk) * 8;
+  const int b = bh / a.H, h = bh % a.H;
+  const int t = threadIdx.x;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int count = 0;
+  for (int si = 0; si < a.nseg; ++si) {
+    const QSeg &g = a.seg[si];
+    if (g.kind != 1) continue;
+    for (int run = 0; run < 2; ++run) {
+      const int lo = run ? g.lo1 : g.lo0, hi = run ? g.hi1 : g.hi0;
+      if (hi > lo) count += hi - lo;
+      for (int tok = lo + t; tok < hi; tok += 256) {
+        const __bf16 *p =
+            (const __bf16 *)g.in + b * g.isb + (int64_t)tok * g.isn + h * g.ish + ch;
+        const bf16x8_t v = *(const bf16x8_t *)p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
+      }
+    }
+  }
+  __shared__ float red[256][9];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[t][i] = acc[i];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[t][i] += red[t + w][i];
+    }
+    __syncthreads();
+  }
+  if (t < 8) a.k_mean[(int64_t)bh * a.D + ch + t] = count ? red[0][t] / (float)count : 0.0f;
+}
+
+__device__ __forceinline__ bool in_runs(const QSeg &g, int tok) {
+  return (tok >= g.lo0 && tok < g.hi0) || (tok >= g.lo1 && tok < g.hi1);
+}
+
+// One workgroup per (tensor, 128-token block, batch, head): 2 threads per token, 64 channels each.
+__global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
+  const int per_bh = a.total_blocks;
+  const int bh = blockIdx.x / per_bh, flat = blockIdx.x % per_bh;
+  const int b = bh / a.H, h = bh % a.H;
+  int si = 0;
+  while (si + 1 < a.nseg && a.seg[si + 1].blk_begin <= flat) ++si;
+  const QSeg &g = a.seg[si];
+  const int blk = flat - g.blk_begin;
+  const int t = threadIdx.x;
+  const int tok = blk * 128 + (t >> 1), c0 = (t & 1) * 64;
+  const bool live = in_runs(g, tok);
+  float x[64];
+  float amax = 0.0f;
+  if (live) {
+    const __bf16 *p = (const __bf16 *)g.in + b * g.isb + (int64_t)tok * g.isn + h * g.ish + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8_t v = *(const bf16x8_t *)(p + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[8 * j + i] = (float)v[i];
+    }
+    if (g.kind == 1) {
+      const float *m = a.k_mean + (int64_t)bh * a.D + c0;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = x[i] - m[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  }
+  if (g.kind == 0 && g.lse) {
+    // the LSE the kernel computes is that of the smoothed scores q.(k - m); record the
+    // per-row shift scale * q.m, which the attention kernel adds back
+    const float *m = a.k_mean + (int64_t)bh * a.D + c0;
+    float dot = 0.0f;
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) dot = fmaf(x[i], m[i], dot);
+    }
+    dot += __shfl_xor(dot, 1);
+    if (live && (t & 1) == 0) g.lse[(int64_t)bh * g.n + tok] = a.softmax_scale * dot;
+  }
+  __shared__ float red[256];
+  red[t] = amax;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
+  }
+  amax = red[0];
+  const float qmax = g.kind == 2 ? 448.0f : 127.0f;
+  const float scale = amax / qmax;
+  const float inv = amax > 0.0f ? qmax / amax : 0.0f;
+  if (t == 0) {
+    g.scale[(int64_t)bh * g.nblk + blk] = scale;
+    if (g.kind == 2) atomicMax((unsigned int *)(a.v_absmax + bh), __float_as_uint(scale));
+  }
+  if (!live) return;
+  uint32_t w32[16];
+  if (g.kind == 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i] * inv, x[4 * i + 1] * inv, 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2] * inv, x[4 * i + 3] * inv, v, true);
+      w32[i] = (uint32_t)v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float r = fminf(fmaxf(__builtin_rintf(x[4 * i + j] * inv), -127.0f), 127.0f);
+        v |= ((uint32_t)(int)r & 0xffu) << (8 * j);
+      }
+      w32[i] = v;
+    }
+  }
+  char *o = (char *)g.out + b * g.osb + (int64_t)tok * g.osn + h * g.osh + c0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *(uint4 *)(o + 16 * j) = uint4{w32[4 * j], w32[4 * j + 1], w32[4 * j + 2], w32[4 * j + 3]};
+}
+
+hipError_t launch_quant_lowbit(const QuantArgs &a, bool mean_given, hipStream_t s) {
+  const int nbh = a.batch * a.H;
+  hipLaunchKernelGGL(quant_init_kernel, dim3((nbh + 63) / 64), dim3(64), 0, s, a.v_absmax, nbh);
+  if (!mean_given) hipLaunchKernelGGL(kmean_kernel, dim3(nbh * (a.D / 8)), dim3(256), 0, s, a);
+  if (a.total_blocks > 0)
+    hipLaunchKernelGGL(quant_kernel, dim3(nbh * a.total_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ============================================================== attention
+
+namespace lb {
+constexpr int D = 128;
+constexpr int BN = 64;                          // keys per tile
+constexpr int ROWB = D;                         // bytes per K/V row (1-byte codes)
+constexpr int CH = ROWB / 16;                   // 16-byte chunks per row (8)
+constexpr int TILEB = BN * ROWB;                // 8 KB
+constexpr int LOADS = TILEB / (256 * 16);       // 2 direct loads per thread per tile
+// chunk c of row r lives at chunk c ^ ((r >> 1) % 8): 16-lane ds_read_b128 of K (16 rows) and
+// the transposing reads of V (8 rows x two 8-byte halves) land on distinct banks
+__device__ __forceinline__ int sw(int r) { return (r >> 1) & (CH - 1); }
+}  // namespace lb
+
+__global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
+  using namespace lb;
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
+
+  const DevWork w = cload<DevWork>((const cWork *)a.work + blockIdx.x);
+  if (w.tile < 0) return;
+  const DevTile tile = cload<DevTile>((const cTile *)a.tiles + w.tile);
+  const int b = w.bh / a.H, h = w.bh - (w.bh / a.H) * a.H;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int T = a.T;
+
+  // ---- Q codes (B operand of S^T): lane holds row l32 of its wave, channels ds*32 + 16*hl + 0..15
+  const int qloc = wave * 32 + l32;
+  const bool qvalid = qloc < tile.rows;
+  const int qrow = tile.row0 + qloc;
+  const Seg qs = a.q[tile.q_kind];
+  i32x4_t qreg[4];
+  {
+    const char *qp = (const char *)qs.p + b * qs.sb + (int64_t)qrow * qs.sn + h * qs.sh;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qreg[ds] = qvalid ? *(const i32x4_t *)(qp + ds * 32 + 16 * hl) : i32x4_t{0, 0, 0, 0};
+  }
+  // Q tiles are 128-row aligned: one Q block per workgroup
+  const float sq = *((const cFloat *)qs.scale + (int64_t)w.bh * qs.nblk + tile.row0 / 128);
+  const float U = *((const cFloat *)a.v_absmax + w.bh);
+  const float cq = sq * a.c;  // times sk gives the log2-domain scale of an int score
+  const int fq = qrow / T;
+
+  // ---- LDS read offsets
+  int koff[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hl) ^ sw(l32)) * 16);
+  // V^T operand via ds_read_b64_tr_b8: in 16-lane group g, lane i reads 8 bytes of row
+  // key(g/2, 8t + i/2), channels db*32 + (g%2)*16 + 8*(i%2) .. +7, for t = 0..3.
+  int voff[4][4];
+  {
+    const int i = lane & 15, g = lane >> 4;
+    const int hv = g >> 1, gh = g & 1, sp = i >> 1, u = i & 1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int s = 8 * t + sp, kb = s >> 4, r = s & 15;
+      const int row = kb * 32 + (r >> 2) * 8 + 4 * hv + (r & 3);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        voff[t][db] = row * ROWB + (((2 * db + gh) ^ sw(row)) * 16) + 8 * u;
+    }
+  }
+  int lrow[LOADS], lcb[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int p = (4 * j + wave) * 64 + lane;
+    lrow[j] = p / CH;
+    lcb[j] = ((p % CH) ^ sw(lrow[j])) * 16;
+  }
+
+  // ---- cursors: tiles never straddle a 128-token block; a range's first tile runs to the next
+  // 64-key boundary, the following ones are aligned
+  const cRange *rng = (const cRange *)a.ranges + tile.r_begin;
+  const int nr = tile.r_count;
+  struct Cur {
+    int r, k, kend, begin, end, mask, param, seg;
+    uint64_t base;  // byte address of (b, key 0, h) of the range's K or V codes
+    uint32_t sn;    // bytes between consecutive keys
+  };
+  auto set_end = [&](Cur &c) { c.kend = min(c.end, (c.k & ~(BN - 1)) + BN); };
+  auto enter = [&](Cur &c, int r, int kind) {
+    while (r < nr && rng[r].begin >= rng[r].end) ++r;
+    c.r = r;
+    if (r >= nr) return;
+    const DevRange R = cload<DevRange>(rng + r);
+    c.k = c.begin = R.begin;
+    c.end = R.end;
+    c.mask = R.mask;
+    c.param = R.param;
+    c.seg = R.seg;
+    set_end(c);
+    if (kind) {
+      const Seg sg = kind == 2 ? a.v[R.seg] : a.k[R.seg];
+      c.base = (uint64_t)sg.p + (uint64_t)((int64_t)b * sg.sb + (int64_t)h * sg.sh);
+      c.sn = (uint32_t)sg.sn;
+    }
+  };
+  auto next = [&](Cur &c, int kind) {
+    if (c.r >= nr) return;
+    c.k = c.kend;
+    if (c.k >= c.end)
+      enter(c, c.r + 1, kind);
+    else
+      set_end(c);
+  };
+  auto tile_rsrc = [&](const Cur &c) {
+    const bool live = c.r < nr;
+    const uint64_t ub = c.base + (uint64_t)(uint32_t)c.k * c.sn;
+    return make_rsrc(ub, live ? (int)((c.kend - c.k) * c.sn) : 0);
+  };
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t sn, char *buf, int j) {
+    const uint32_t off = (uint32_t)lrow[j] * sn + lcb[j];
+    lds_char *dst = (lds_char *)buf + (4 * j + wave) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
+                                             (int)off, 0, 0, 0);
+  };
+  auto issue = [&](const Cur &c, char *buf) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) load_one(rs, c.sn, buf, j);
+  };
+  // per-tile scales of the tile at cursor c: log2-domain score factor and the V weight
+  auto tile_scales = [&](const Cur &c, float &fk, float &wv) {
+    const Seg ks = a.k[c.seg], vs = a.v[c.seg];
+    const int blk = c.k >> 7;
+    const float sk = *((const cFloat *)ks.scale + (int64_t)w.bh * ks.nblk + blk);
+    const float sv = *((const cFloat *)vs.scale + (int64_t)w.bh * vs.nblk + blk);
+    fk = fmaxf(cq * sk, 1e-30f);  // an all-zero Q or K block: scores 0, masks stay -inf
+    wv = U > 0.0f ? 448.0f * sv / U : 0.0f;
+  };
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
+  float m_run = -__builtin_inff();
+  float l_part = 0.0f;
+
+  auto qk = [&](const char *kbuf, i32x16_t &s0, i32x16_t &s1) {
+    const lds_char *Kl = (const lds_char *)kbuf;
+    s0 = i32x16_t{};
+    s1 = i32x16_t{};
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const i32x4_t a0 = *(const i32x4_t *)(Kl + koff[ds]);
+      const i32x4_t a1 = *(const i32x4_t *)(Kl + 32 * ROWB + koff[ds]);
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[ds], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[ds], s1, 0, 0, 0);
+    }
+  };
+
+  // softmax + PV of the tile at cursor c with integer scores (s0, s1) and V in `vbuf`
+  auto softmax_pv = [&](const Cur &c, const i32x16_t &s0, const i32x16_t &s1, const char *vbuf) {
+    float fk, wv;
+    tile_scales(c, fk, wv);
+    float x0[16], x1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x0[i] = (float)s0[i];
+      x1[i] = (float)s1[i];
+    }
+    if (c.mask != FA_MASK_NONE || c.kend - c.k < BN) {
+      int klo = c.begin, khi = c.kend;
+      if (c.mask == FA_MASK_SAME_FRAME) {
+        klo = max(klo, fq * T);
+        khi = min(khi, (fq + 1) * T);
+      } else if (c.mask == FA_MASK_GATE && fq < c.param) {
+        khi = klo;
+      }
+      const int base = c.k + 4 * hl;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k0i = base + (i >> 2) * 8 + (i & 3);
+        const int k1i = k0i + 32;
+        if (k0i < klo || k0i >= khi) x0[i] = -__builtin_inff();
+        if (k1i < klo || k1i >= khi) x1[i] = -__builtin_inff();
+      }
+    }
+    float mx = fmaxf(x0[0], x0[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, x0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x1[i]);
+    mx = xhalf_max(mx);
+    const float mt = mx * fk;  // fk > 0
+    const bool need = mt > m_run;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+    m_run = need ? mt : m_run;
+    l_part *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+    }
+    const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
+    i32x8_t pw;  // P^T: byte kb*16 + r of the lane's 32 keys
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(fmaf(x0[i + j], fk, mneg));
+        e[4 + j] = __builtin_amdgcn_exp2f(fmaf(x1[i + j], fk, mneg));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) l_part += e[j];
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0] * wv, e[1] * wv, 0, false);
+      pw[i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2] * wv, e[3] * wv, v, true);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4] * wv, e[5] * wv, 0, false);
+      pw[4 + i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[6] * wv, e[7] * wv, v, true);
+    }
+    const lds_char *Vl = (const lds_char *)vbuf;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x8_t av;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t *)(Vl + voff[t][db]));
+        av[2 * t] = r2[0];
+        av[2 * t + 1] = r2[1];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pw, oacc[db], 0, 0, 0, 127, 0,
+                                                                 127);
+    }
+  };
+
+  auto end_step = [&]() {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  Cur cc, ck, cv;  // tile j; K prefetch (j+2); V prefetch (j+1)
+  enter(cc, 0, 0);
+  if (cc.r < nr) {
+    Cur k0c, k1c;
+    enter(k0c, cc.r, 1);
+    k1c = k0c;
+    next(k1c, 1);
+    enter(cv, cc.r, 2);
+    issue(k0c, kbuf0);
+    issue(cv, vbuf0);
+    if (k1c.r < nr) issue(k1c, kbuf1);
+    next(cv, 2);
+    ck = k1c;
+    next(ck, 1);
+    end_step();
+    i32x16_t sa0, sa1, sb0, sb1;
+    qk(kbuf0, sa0, sa1);
+    while (true) {
+      // even step: S_j in (sa); K of j+1 in kbuf1, V of j in vbuf0
+      if (ck.r < nr) issue(ck, kbuf0);
+      if (cv.r < nr) issue(cv, vbuf1);
+      qk(kbuf1, sb0, sb1);
+      softmax_pv(cc, sa0, sa1, vbuf0);
+      end_step();
+      if (cv.r >= nr) break;
+      next(cc, 0); next(cv, 2); next(ck, 1);
+      // odd step
+      if (ck.r < nr) issue(ck, kbuf1);
+      if (cv.r < nr) issue(cv, vbuf0);
+      qk(kbuf0, sa0, sa1);
+      softmax_pv(cc, sb0, sb1, vbuf1);
+      end_step();
+      if (cv.r >= nr) break;
+      next(cc, 0); next(cv, 2); next(ck, 1);
+    }
+  }
+
+  // ---- epilogue: O = (U/448) O^T / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = xhalf_sum(l_part);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.0f ? (U / 448.0f) / l_tot : 0.0f;
+  const Seg os = a.o[tile.q_kind];
+  __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t v;
+      v[0] = (__bf16)(oacc[db][g * 4 + 0] * inv);
+      v[1] = (__bf16)(oacc[db][g * 4 + 1] * inv);
+      v[2] = (__bf16)(oacc[db][g * 4 + 2] * inv);
+      v[3] = (__bf16)(oacc[db][g * 4 + 3] * inv);
+      *(bf16x4_t *)(op + db * 32 + g * 8 + 4 * hl) = v;
+    }
+  }
+  float *lse = a.lse[tile.q_kind];
+  if (lse && hl == 0) {
+    // lse holds the smoothing shift scale * q.m written by the quantiser
+    float *lp = lse + (int64_t)w.bh * a.q_rows[tile.q_kind] + qrow;
+    *lp = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f + *lp
+                       : -__builtin_inff();
+  }
+}
+
+hipError_t launch_attn_lowbit(const AttnArgs &a, int head_dim, int grid, hipStream_t s) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_lowbit_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace fa
-
-extern "C" fa_status fa_quantize_lowbit(const fa_layout *, const fa_io *, const fa_io *, int32_t,
-                                        fa_hip_stream) {
-  return FA_ERR_UNSUPPORTED;
-}

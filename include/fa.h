@@ -197,6 +197,11 @@ fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream)
  *    out->v_absmax.
  * Codes go to out->{q,k,v}_* .data (same strides as declared there), scales
  * to their .scale arrays.  Ring frames outside the call's view are not read.
+ * Smoothing shifts every score of a row by scale*q.m, which leaves O unchanged
+ * but not the LSE: for each query kind whose out->lse_* is non-NULL the
+ * quantiser writes that per-row shift there, and fa_attn_fwd on the low-bit
+ * layout adds it to the LSE it computes.  Pass the same lse_* buffers to both
+ * calls (or NULL to both).
  */
 enum { FA_QUANT_MEAN_GIVEN = 1 };
 fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out, int32_t flags,

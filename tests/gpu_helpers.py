@@ -60,6 +60,8 @@ def tol_check(got, want, dtype: str, what: str, lse_got=None, lse_want=None):
         st["cos"] = cos
         say("  %s: cosine %.6f" % (what, cos))
         assert cos >= 0.999 and st["max"] <= 5e-2, (what, st)
+        if "lse_max" in st:  # diagnostic bound: a wrong mask moves LSE by ~0.05
+            assert st["lse_max"] <= 2e-2, (what, st)
     return st
 
 
@@ -113,6 +115,7 @@ class Call:
 
 def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tokens=(),
                 ref_t0=(), query_rows=7, scale_k=1.0) -> Call:
+    """Seeded N(0,1) inputs (bf16-rounded unless fp32) for one call."""
     g = np.random.default_rng(seed)
 
     def n(*shape):

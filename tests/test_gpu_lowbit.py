@@ -1,0 +1,226 @@
+"""Low-bit path on the GPU: the quantiser against the oracle's (codes and scales
+bit for bit, given the same key mean), and the int8/e4m3 attention against the
+fp32 oracle on the unquantised inputs (cosine >= 0.999, max|dO| <= 5e-2), with
+a per-channel N(0, 4) key offset to stress the mean smoothing."""
+import numpy as np
+import pytest
+import torch
+
+import fa_workloads as W
+import gpu_helpers as G
+from frame_aligned_attention_amd import binding as B
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+TGT, SRC, REF = G.TGT, G.SRC, G.REF
+
+
+def lowbit_call(seed, T, C, H, cs=0, window=0, cache=0, refs=(), t0s=(), query_rows=1,
+                offset_sd=2.0):
+    c = G.random_call(seed, T, C, H, 128, "lowbit", cs=cs, window=window, cache=cache,
+                      ref_tokens=refs, ref_t0=t0s, query_rows=query_rows)
+    off = np.random.default_rng(seed + 1000).standard_normal((H, 128)).astype(np.float32) * offset_sd
+    for name in ("k_hist", "k_src", "k_ref"):
+        setattr(c, name, W.round_bf16(getattr(c, name) + off[None]))
+    return c
+
+
+def nblk(n):
+    return (n + 127) // 128
+
+
+class LowbitRun:
+    """bf16 inputs of a Call, code/scale buffers, fa_quantize_lowbit + fa_attn_fwd."""
+
+    def __init__(self, c: G.Call):
+        self.c = c
+        self.desc = c.desc()
+        self.L = B.fa_layout_build(self.desc, c.ring_first)
+        t = {}
+        if TGT in c.kinds():
+            t["q_tgt"] = G.dev(c.q[TGT])
+        if SRC in c.kinds():
+            t["q_src"] = G.dev(c.q[SRC])
+        if REF in c.kinds() and sum(c.ref_tokens):
+            t["q_ref"] = G.dev(c.q[REF])
+        own = (c.cs - c.hist_first) * c.T
+        t["k_tgt"], t["v_tgt"] = G.dev(c.k_hist[own:]), G.dev(c.v_hist[own:])
+        t["k_src"], t["v_src"] = G.dev(c.k_src), G.dev(c.v_src)
+        if sum(c.ref_tokens):
+            t["k_ref"], t["v_ref"] = G.dev(c.k_ref), G.dev(c.v_ref)
+        if c.cache:
+            t["k_ring"], t["v_ring"] = G.ring_tensors(c, torch.bfloat16)
+        self.inp = t
+        self.codes, self.scales = {}, {}
+        for n, x in t.items():
+            dt = torch.uint8 if n.startswith("v_") else torch.int8
+            self.codes[n] = torch.zeros(x.shape, dtype=dt, device="cuda")
+            self.scales[n] = torch.zeros((1, c.H, nblk(x.shape[1])), dtype=torch.float32,
+                                         device="cuda")
+        self.k_mean = torch.zeros((1, c.H, 128), dtype=torch.float32, device="cuda")
+        self.v_absmax = torch.zeros((1, c.H), dtype=torch.float32, device="cuda")
+        # outputs; the quantiser writes the per-row smoothing shift into the LSE buffers
+        rows = {TGT: c.C * c.T, SRC: c.C * c.T, REF: sum(c.ref_tokens)}
+        self.out = {}
+        for k in c.kinds():
+            if rows[k] == 0:
+                continue
+            nm = G.KIND_NAMES[k]
+            self.out["o_" + nm] = torch.zeros((1, rows[k], c.H, 128), dtype=torch.bfloat16,
+                                              device="cuda")
+            self.out["lse_" + nm] = torch.zeros((1, c.H, rows[k]), dtype=torch.float32,
+                                                device="cuda")
+
+    def quantize(self, mean=None):
+        flags = 0
+        if mean is not None:
+            self.k_mean.copy_(torch.from_numpy(mean).reshape(1, *mean.shape))
+            flags = B.FA_QUANT_MEAN_GIVEN
+        io_in = B.make_io(self.inp)
+        lses = {n: x for n, x in self.out.items() if n.startswith("lse_")}
+        io_out = B.make_io({**self.codes, **lses, "k_mean": self.k_mean,
+                            "v_absmax": self.v_absmax}, self.scales)
+        B.fa_quantize_lowbit(self.L, io_in, io_out, flags)
+        torch.cuda.synchronize()
+
+    def attend(self):
+        c = self.c
+        io = B.make_io({**self.codes, **self.out, "v_absmax": self.v_absmax}, self.scales)
+        B.fa_attn_fwd(self.L, io)
+        torch.cuda.synchronize()
+        return {k: (G.host(self.out["o_" + G.KIND_NAMES[k]])[0],
+                    G.host(self.out["lse_" + G.KIND_NAMES[k]])[0])
+                for k in c.kinds() if "o_" + G.KIND_NAMES[k] in self.out}
+
+
+def visible_keys(c: G.Call):
+    """Host copies of the key tensors as the quantiser sees them: ring slots out of view zeroed,
+    and the token mask of what is in view."""
+    segs = {}
+    own = (c.cs - c.hist_first) * c.T
+    segs["k_tgt"], segs["v_tgt"] = c.k_hist[own:], c.v_hist[own:]
+    segs["k_src"], segs["v_src"] = c.k_src, c.v_src
+    if sum(c.ref_tokens):
+        segs["k_ref"], segs["v_ref"] = c.k_ref, c.v_ref
+    masks = {n: np.ones(x.shape[0], bool) for n, x in segs.items()}
+    if c.cache:
+        cap, T = c.cache, c.T
+        for n, src in (("k_ring", c.k_hist), ("v_ring", c.v_hist)):
+            r = np.zeros((cap * T, c.H, 128), np.float32)
+            m = np.zeros(cap * T, bool)
+            for g in range(c.hist_first, c.cs):
+                s = g % cap
+                i = (g - c.hist_first) * T
+                r[s * T:(s + 1) * T] = src[i:i + T]
+                m[s * T:(s + 1) * T] = True
+            segs[n], masks[n] = r, m
+    return segs, masks
+
+
+QUANT_CASES = [
+    # seed, T, C, H, cs, window, cache, refs, t0, query rows
+    (41, 50, 3, 2, 9, 4, 5, [20], [0], 1),       # ring wraps; partial 128-blocks everywhere
+    (42, 40, 3, 3, 0, 0, 0, [16, 30], [0, 1], 7),  # bidirectional, all query kinds
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=["q%d" % c[0] for c in QUANT_CASES])
+def test_quantiser_codes_match_oracle(case):
+    seed, T, C, H, cs, win, cap, refs, t0s, qr = case
+    G.say("case: quantiser codes %s" % (case,))
+    c = lowbit_call(seed, T, C, H, cs, win, cap, refs, t0s, qr)
+    run = LowbitRun(c)
+    segs, masks = visible_keys(c)
+    mean = O.kmean([segs[n][masks[n]] for n in segs if n.startswith("k_")])
+    if "k_ring" in segs:  # out-of-view ring tokens: x - m = 0 there, so they do not move absmax
+        segs["k_ring"][~masks["k_ring"]] = mean[None]
+    run.quantize(mean=mean)
+    for n, x in list(segs.items()) + [("q_" + G.KIND_NAMES[k], c.q[k]) for k in c.kinds()
+                                      if c.q[k].shape[0]]:
+        msk = masks.get(n, np.ones(x.shape[0], bool))
+        if n.startswith("v_"):
+            codes, scales = O.quant_e4m3(x)
+        else:
+            codes, scales = O.quant_int8(x, mean=mean if n.startswith("k_") else None)
+        got = run.codes[n].cpu().numpy()[0]
+        got_s = run.scales[n].cpu().numpy()[0]
+        assert np.array_equal(got_s, scales), n
+        assert np.array_equal(got[msk], codes[msk].view(got.dtype)), n
+    want_absmax = np.max(np.stack([O.quant_e4m3(segs[n])[1].max(1) for n in segs
+                                   if n.startswith("v_")]), 0)
+    assert np.array_equal(run.v_absmax.cpu().numpy()[0], want_absmax)
+    # the device mean (no FA_QUANT_MEAN_GIVEN) agrees with the oracle's to fp32 rounding
+    run.quantize(mean=None)
+    np.testing.assert_allclose(run.k_mean.cpu().numpy()[0], mean, rtol=2e-5, atol=2e-6)
+
+
+ATTN_CASES = [
+    # seed, T, C, H, cs, window, cache, refs, t0, query rows
+    (51, 50, 3, 2, 9, 4, 5, [20], [0], 1),
+    (52, 160, 3, 2, 0, 0, 0, [96, 64], [0, 1], 7),  # all query kinds (source rows: 160+ keys)
+    (53, 130, 3, 2, 12, 9, 9, [64, 64], [0, 13], 1),  # gate inside the chunk
+    (54, 100, 2, 1, 3, 0, 4, [200], [0], 3),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=["a%d" % c[0] for c in ATTN_CASES])
+def test_lowbit_attention_against_fp32_oracle(case):
+    seed, T, C, H, cs, win, cap, refs, t0s, qr = case
+    G.say("case: low-bit attention %s" % (case,))
+    c = lowbit_call(seed, T, C, H, cs, win, cap, refs, t0s, qr)
+    run = LowbitRun(c)
+    run.quantize()
+    res = run.attend()
+    ref = G.oracle_all(c)
+    for k, (o, lse) in res.items():
+        G.tol_check(o, ref[k][0], "lowbit", "lowbit %s rows" % G.KIND_NAMES[k], lse, ref[k][1])
+
+
+def lowbit_stream_chunk_call(cs, H):
+    """A chunk of the low-bit streaming workload (N(0,4) key offset) with its history."""
+    w = W.WORKLOADS[4]
+    lo = max(0, cs - w.window)
+    c = G.Call(T=w.T, C=w.C, H=H, D=w.D, dtype="lowbit", cs=cs, window=w.window,
+               cache=w.cache_frames, ref_tokens=list(w.ref_tokens), ref_t0=list(w.ref_t0),
+               query_rows=1, hist_first=lo)
+    ks, vs = [], []
+    for ch in range(lo // w.C, cs // w.C + 1):
+        x = W.chunk_tensors(w, ch, H=H)
+        ks.append(x["k_tgt"]); vs.append(x["v_tgt"])
+    c.k_hist = np.concatenate(ks)
+    c.v_hist = np.concatenate(vs)
+    x = W.chunk_tensors(w, cs // w.C, H=H)
+    r = W.ref_tensors(w, H=H)
+    c.q = {TGT: x["q_tgt"]}
+    c.k_src, c.v_src = x["k_src"], x["v_src"]
+    c.k_ref, c.v_ref = r["k_ref"], r["v_ref"]
+    return c
+
+
+def test_lowbit_workload_steady_chunk_sampled():
+    G.say("case: low-bit workload, steady chunk (cs = 57), 40 heads, sampled rows")
+    c = lowbit_stream_chunk_call(57, 40)
+    run = LowbitRun(c)
+    run.quantize()
+    res = run.attend()
+    p = c.problem()
+    o, lse = res[TGT]
+    rows = G.sample_rows(c, TGT, 64)
+    heads = [0, 17, 39]
+    kk = [TGT] * (len(rows) * len(heads))
+    hh = [h for h in heads for _ in rows]
+    rr = [int(r) for _ in heads for r in rows]
+    ro, rl = O.attn_rows(p, kk, hh, rr)
+    go = np.stack([o[r, h] for h, r in zip(hh, rr)])
+    gl = np.array([lse[h, r] for h, r in zip(hh, rr)])
+    G.tol_check(go, ro, "lowbit", "lowbit steady chunk (sampled %d)" % len(rr), gl, rl)
+
+
+def test_lowbit_workload_warmup_chunk_full():
+    G.say("case: low-bit workload, chunk 2 (cs = 6, ring partly filled), 1 head, every row")
+    c = lowbit_stream_chunk_call(6, 1)
+    run = LowbitRun(c)
+    run.quantize()
+    res = run.attend()
+    ref = G.oracle_all(c)
+    G.tol_check(res[TGT][0], ref[TGT][0], "lowbit", "lowbit chunk 2", res[TGT][1], ref[TGT][1])
