@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_I8_F8_TOPS = 5000.0    # MI355X dense int8 / fp8 MFMA
 METRIC = "frame-aligned attn useful TFLOP/s + ms per streaming chunk, 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_stream1560_h40_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "frame_aligned_attention_amd", "csrc", "fa_attn_bf16.hip")
@@ -186,6 +187,58 @@ def time_single_call(wid, torch, W, B, reps=10):
     return {"workload": w.name, "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
             "useful_tflops": round(fl / med / 1e9, 2),
             "mfma_frac": round(fl / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def time_lowbit_chunk(torch, W, B, reps=10):
+    """Low-bit workload, steady chunk (cs = 57): quantiser + int8/fp8 attention, and the
+    attention alone; useful ops against the dense int8/fp8 MFMA peak."""
+    w = W.WORKLOADS[4]
+    cs = (w.chunks - 1) * w.C
+    dev = lambda x: torch.from_numpy(x).unsqueeze(0).to("cuda").to(torch.bfloat16).contiguous()
+    x = W.chunk_tensors(w, cs // w.C)
+    r = W.ref_tensors(w)
+    t = {n: dev(v) for n, v in {**x, **r}.items()}
+    for n in ("k_ring", "v_ring"):
+        t[n] = (torch.randn((1, w.cache_frames * w.T, w.H, w.D), device="cuda") * 1.0).to(torch.bfloat16)
+    d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=cs,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=1, dtype=B.FA_LOWBIT)
+    L = B.fa_layout_build(d)
+    codes, scales = {}, {}
+    for n, v in t.items():
+        codes[n] = torch.empty(v.shape, dtype=torch.uint8 if n.startswith("v_") else torch.int8,
+                               device="cuda")
+        scales[n] = torch.empty((1, w.H, (v.shape[1] + 127) // 128), dtype=torch.float32,
+                                device="cuda")
+    rows = w.C * w.T
+    out = {"o_tgt": torch.empty((1, rows, w.H, w.D), dtype=torch.bfloat16, device="cuda"),
+           "lse_tgt": torch.empty((1, w.H, rows), dtype=torch.float32, device="cuda"),
+           "k_mean": torch.empty((1, w.H, w.D), dtype=torch.float32, device="cuda"),
+           "v_absmax": torch.empty((1, w.H), dtype=torch.float32, device="cuda")}
+    io_in = B.make_io(t)
+    io_q = B.make_io({**codes, "lse_tgt": out["lse_tgt"], "k_mean": out["k_mean"],
+                      "v_absmax": out["v_absmax"]}, scales)
+    io_a = B.make_io({**codes, **out}, scales)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.fa_quantize_lowbit(L, io_in, io_q, 0, stream)
+        B.fa_attn_fwd(L, io_a, stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        B.fa_quantize_lowbit(L, io_in, io_q, 0, stream)
+        e[1].record(stream)
+        B.fa_attn_fwd(L, io_a, stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = statistics.median([e[0].elapsed_time(e[1]) for e in ev])
+    a_ms = statistics.median([e[1].elapsed_time(e[2]) for e in ev])
+    ops = B.fa_layout_stats(L)["useful_flops"]
+    return {"workload": w.name + " (steady chunk, cs=57)", "quantise_ms": round(q_ms, 4),
+            "attn_ms": round(a_ms, 4), "chunk_ms": round(q_ms + a_ms, 4),
+            "attn_useful_tops": round(ops / a_ms / 1e9, 2),
+            "attn_frac_of_5000_tops": round(ops / a_ms / 1e9 / PEAK_I8_F8_TOPS, 4),
+            "chunk_useful_tops": round(ops / (q_ms + a_ms) / 1e9, 2)}
 
 
 def cpu_baseline(W, budget_s):
@@ -379,7 +432,8 @@ def main():
     }
     if not args.no_extra:
         log("bench: other bf16 workloads")
-        out["other_workloads"] = [time_single_call(1, torch, W, B), time_single_call(3, torch, W, B)]
+        out["other_workloads"] = [time_single_call(1, torch, W, B), time_single_call(3, torch, W, B),
+                                  time_lowbit_chunk(torch, W, B)]
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)

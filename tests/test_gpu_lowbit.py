@@ -224,3 +224,52 @@ def test_lowbit_workload_warmup_chunk_full():
     res = run.attend()
     ref = G.oracle_all(c)
     G.tol_check(res[TGT][0], ref[TGT][0], "lowbit", "lowbit chunk 2", res[TGT][1], ref[TGT][1])
+
+
+def test_lowbit_stream_through_driver():
+    """Six chunks of the low-bit workload (2 heads) through fa_stream_layout, fa_quantize_lowbit,
+    fa_attn_fwd and fa_stream_advance (the bf16 ring is appended by the driver)."""
+    G.say("case: low-bit stream, 6 chunks, 2 heads")
+    w = W.WORKLOADS[4]
+    H = 2
+    d = B.make_desc(w.C, w.T, H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=0,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=1, dtype=B.FA_LOWBIT)
+    s = B.Stream(d)
+    ring = {n: torch.zeros((1, w.cache_frames * w.T, H, w.D), dtype=torch.bfloat16, device="cuda")
+            for n in ("k_ring", "v_ring")}
+    r = W.ref_tensors(w, H=H)
+    ks, vs = [], []
+    for ch in range(6):
+        x = W.chunk_tensors(w, ch, H=H)
+        t = {"q_tgt": G.dev(x["q_tgt"]), "k_tgt": G.dev(x["k_tgt"]), "v_tgt": G.dev(x["v_tgt"]),
+             "k_src": G.dev(x["k_src"]), "v_src": G.dev(x["v_src"]),
+             "k_ref": G.dev(r["k_ref"]), "v_ref": G.dev(r["v_ref"]), **ring}
+        codes = {n: torch.empty(v.shape, dtype=torch.uint8 if n.startswith("v_") else torch.int8,
+                                device="cuda") for n, v in t.items()}
+        scales = {n: torch.empty((1, H, nblk(v.shape[1])), dtype=torch.float32, device="cuda")
+                  for n, v in t.items()}
+        rows = w.C * w.T
+        out = {"o_tgt": torch.empty((1, rows, H, w.D), dtype=torch.bfloat16, device="cuda"),
+               "lse_tgt": torch.empty((1, H, rows), dtype=torch.float32, device="cuda"),
+               "k_mean": torch.empty((1, H, w.D), dtype=torch.float32, device="cuda"),
+               "v_absmax": torch.empty((1, H), dtype=torch.float32, device="cuda")}
+        L = s.layout()
+        B.fa_quantize_lowbit(L, B.make_io(t), B.make_io({**codes, "lse_tgt": out["lse_tgt"],
+                                                         "k_mean": out["k_mean"],
+                                                         "v_absmax": out["v_absmax"]}, scales))
+        B.fa_attn_fwd(L, B.make_io({**codes, **out}, scales))
+        s.advance(B.make_io(t))
+        torch.cuda.synchronize()
+        ks.append(x["k_tgt"]); vs.append(x["v_tgt"])
+        cs = ch * w.C
+        lo = max(0, cs - w.window)
+        c = G.Call(T=w.T, C=w.C, H=H, D=w.D, dtype="lowbit", cs=cs, window=w.window,
+                   cache=w.cache_frames, ref_tokens=list(w.ref_tokens), ref_t0=list(w.ref_t0),
+                   query_rows=1, hist_first=lo)
+        c.k_hist = np.concatenate(ks[lo // w.C:])
+        c.v_hist = np.concatenate(vs[lo // w.C:])
+        c.q = {TGT: x["q_tgt"]}
+        c.k_src, c.v_src, c.k_ref, c.v_ref = x["k_src"], x["v_src"], r["k_ref"], r["v_ref"]
+        G.compare_sampled(c, {TGT: (G.host(out["o_tgt"])[0], G.host(out["lse_tgt"])[0])},
+                          n_rows=32, what="lowbit stream chunk %d" % ch)
+    assert s.state() == (18, 6)
