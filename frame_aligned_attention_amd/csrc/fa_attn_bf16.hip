@@ -231,13 +231,36 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 
   // One pipeline step: softmax and PV of the tile whose scores are in (s0, s1) and whose V
   // sits in LDS buffer `vbuf`, while S of the next tile (K in LDS buffer `kbuf`) accumulates in
-  // (n0, n1).  The MFMAs of the next S are independent of the softmax, and the scheduling
-  // hints interleave them with its VALU work.
+  // (n0, n1) and the direct loads of K (two tiles ahead, cursor kc -> kdst) and V (one tile
+  // ahead, cursor vc -> vdst) are issued.  The row max and the (rare) O rescale come first;
+  // the rest is one branch-free region whose instruction order the scheduling hints set:
+  // operand reads run a few MFMAs ahead, the exp work of this tile hides under the MFMAs of
+  // the next S, and the direct loads trickle in one every other MFMA.
   auto step = [&](f32x16_t &s0, f32x16_t &s1, f32x16_t &n0, f32x16_t &n1, const char *kbuf,
                   const char *vbuf, const Cur &kc, char *kdst, const Cur &vc, char *vdst) {
+    // ---- row max of this tile (in-lane over 32 scores, then across the lane halves)
+    float mx = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s0[i]), s0[i + 1]);
+    mx = fmaxf(fmaxf(mx, s0[15]), s1[0]);
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), s1[i + 1]);
+    mx = fmaxf(mx, s1[15]);
+    mx = xhalf_max(mx);
+    // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
+    const float mt = mx * c;
+    const bool need = mt > m_run + kThr;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+    m_run = need ? mt : m_run;
+    l_part *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
+    }
+    const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
+
+    // ---- one region
     const lds_char *Kl = (const lds_char *)kbuf;
-    // prefetch of K (two tiles ahead) and V (one tile ahead), one direct load per k-step of the
-    // next S so the loads trickle into the memory pipeline instead of arriving in one burst
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
     auto prefetch = [&](int ds) {
 #pragma unroll
@@ -248,37 +271,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
           load_one(vrs, vc.sn2, true, vdst, li - Cfg::LOADS);
       }
     };
-    n0 = f32x16_t{};
-    n1 = f32x16_t{};
-    qk_step(Kl, 0, n0, n1);
-    prefetch(0);
-    qk_step(Kl, 1, n0, n1);
-    prefetch(1);
-    // row max of this tile (in-lane over 32 scores, then across the lane halves)
-    float mx = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s0[i]), s0[i + 1]);
-    mx = fmaxf(fmaxf(mx, s0[15]), s1[0]);
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), s1[i + 1]);
-    mx = fmaxf(mx, s1[15]);
-    qk_step(Kl, 2, n0, n1);
-    prefetch(2);
-    mx = xhalf_max(mx);
-    // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
-    const float mt = mx * c;
-    const bool need = mt > m_run + kThr;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-    m_run = need ? mt : m_run;
-    l_part *= alpha;
-    const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
     u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      if ((i == 4 || i == 8 || i == 12) && 2 + i / 4 < Cfg::DS) {
-        qk_step(Kl, 2 + i / 4, n0, n1);
-        prefetch(2 + i / 4);
-      }
       const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
                            (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i + 1], c, mneg))};
       const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg)),
@@ -288,25 +283,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
       pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e0);
       pw[2 + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e1);
     }
-    if (Cfg::DS > 6) {
-      qk_step(Kl, 6, n0, n1);
-      prefetch(6);
-    }
-    if (Cfg::DS > 7) {
-      qk_step(Kl, 7, n0, n1);
-      prefetch(7);
-    }
-    // interleave: per MFMA of the next S, a slice of the softmax VALU, and a direct load every
-    // other MFMA
+    n0 = f32x16_t{};
+    n1 = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < 2 * Cfg::DS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-    }
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
+    for (int ds = 0; ds < Cfg::DS; ++ds) {
+      qk_step(Kl, ds, n0, n1);
+      prefetch(ds);
     }
     // O^T += V^T . P^T
     const lds_char *Vl = (const lds_char *)vbuf;
@@ -324,6 +306,25 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             av, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[db], 0, 0, 0);
       }
+    }
+    // schedule of the region (groups are filled in order, dependencies permitting):
+    // K operand reads two k-steps ahead; per QK MFMA a share of the exp VALU and every other
+    // MFMA one direct load; V operand reads four PV MFMAs ahead.
+    constexpr int NQK = 2 * Cfg::DS, NPV = 4 * Cfg::DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read: K operands of k-steps 0, 1
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK)
+      if (i + 4 < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read: V operands of PV 0..3
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
+      if (i + 4 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (rest of the softmax)
     }
   };
 
