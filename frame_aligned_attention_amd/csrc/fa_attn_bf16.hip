@@ -259,7 +259,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     }
     const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
 
-    // ---- one region
+    // ---- one region.  While a wave is in it, raise its priority: of the two waves sharing
+    // a SIMD the one in its MFMA-dense region wins issue, and the other's row-max / barrier
+    // work fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     const lds_char *Kl = (const lds_char *)kbuf;
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
     auto prefetch = [&](int ds) {
@@ -331,6 +334,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   // Every wave waits for its own direct loads, then the barrier publishes all of them (and
   // frees the buffers read in this step).
   auto end_step = [&]() {
+    __builtin_amdgcn_s_setprio(0);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
