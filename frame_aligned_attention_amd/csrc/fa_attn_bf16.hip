@@ -50,6 +50,7 @@ struct Bf16Cfg {
   static constexpr int CH = ROWB / 16;          // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
   static constexpr int LOADS = TILEB / (256 * 16);  // 16-byte direct loads per thread per tile
+  static constexpr int RSTEP = 256 * 16 / ROWB;     // rows covered by one load of all lanes
   static constexpr int DS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;             // 32-channel blocks of O^T
   // K: chunk c of row r lives at chunk c ^ (r % CH): a ds_read_b128 of 16 lanes (16 rows, one
@@ -60,16 +61,18 @@ struct Bf16Cfg {
   __device__ static int vsw(int r) { return (4 * r) & (CH - 1); }
 };
 
-// Where each lane's direct loads of a tile land and which bytes of the tile's
-// rows they fetch: load j of wave w writes LDS chunks [(4j + w)*64, +64) of the
-// tile, lane i chunk (4j + w)*64 + i.
+// Where each lane's direct loads of a tile land and which bytes of the tile's rows they fetch:
+// load j of wave w writes LDS chunks [(4j + w)*64, +64) of the tile, lane i chunk
+// (4j + w)*64 + i, i.e. row row0 + j*RSTEP at logical chunk lcb/16 of that row.  RSTEP is a
+// multiple of CH, so the swizzle (a function of the row modulo CH) is the same for every j.
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_map(int j, int w, int lane, int &row, int &lcb) {
+__device__ __forceinline__ void load_map(int w, int lane, int &row0, int &lcb) {
   using Cfg = Bf16Cfg<D>;
-  const int p = (4 * j + w) * 64 + lane;
-  row = p / Cfg::CH;
+  static_assert(Cfg::RSTEP % Cfg::CH == 0, "swizzle must not depend on the load index");
+  const int p = w * 64 + lane;
+  row0 = p / Cfg::CH;
   const int pc = p % Cfg::CH;
-  const int lc = pc ^ (IS_V ? Cfg::vsw(row) : Cfg::ksw(row));
+  const int lc = pc ^ (IS_V ? Cfg::vsw(row0) : Cfg::ksw(row0));
   lcb = lc * 16;
 }
 
@@ -129,13 +132,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
       voff[db] = vrow * ROWB + ((lc ^ Cfg::vsw(vrow)) * 16) + (av & 1) * 8;
     }
   }
-  // direct-load row/column of each of this lane's loads (K and V layouts differ)
-  int krow[Cfg::LOADS], kcb[Cfg::LOADS], vrow_[Cfg::LOADS], vcb[Cfg::LOADS];
-#pragma unroll
-  for (int j = 0; j < Cfg::LOADS; ++j) {
-    load_map<D, false>(j, wave, lane, krow[j], kcb[j]);
-    load_map<D, true>(j, wave, lane, vrow_[j], vcb[j]);
-  }
+  // direct-load row and column of this lane's first load (K and V layouts differ)
+  int krow0, kcb0, vrow0, vcb0;
+  load_map<D, false>(wave, lane, krow0, kcb0);
+  load_map<D, true>(wave, lane, vrow0, vcb0);
 
   // ---- tile cursors over the flattened (range, 64-key tile) sequence.  Each cursor keeps the
   // fields of its current range (and, for the load cursors, the (batch, head) base of the
@@ -179,17 +179,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     const int nvalid = live ? min(BN, c.end - c.k) : 0;
     return make_rsrc(ub, (int)(nvalid * c.sn2));
   };
-  // Direct load j of this lane's share of a K (is_v = false) or V tile into LDS buffer `buf`.
-  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t sn2, bool is_v, char *buf, int j) {
-    const uint32_t off = (uint32_t)(is_v ? vrow_[j] : krow[j]) * sn2 + (is_v ? vcb[j] : kcb[j]);
+  // Direct load j of this lane's share of a tile into LDS buffer `buf`; voff0 is the lane's
+  // byte offset of its first load within the tile (row0 * sn2 + column).
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t voff0, uint32_t sn2, char *buf, int j) {
+    const uint32_t off = voff0 + (uint32_t)(j * Cfg::RSTEP) * sn2;
     lds_char *dst = (lds_char *)buf + (4 * j + wave) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
                                              (int)off, 0, 0, 0);
   };
+  auto lane_off = [&](const Cur &c, bool is_v) {
+    return (uint32_t)(is_v ? vrow0 : krow0) * c.sn2 + (uint32_t)(is_v ? vcb0 : kcb0);
+  };
   auto issue = [&](const Cur &c, bool is_v, char *buf) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c);
+    const uint32_t o = lane_off(c, is_v);
 #pragma unroll
-    for (int j = 0; j < Cfg::LOADS; ++j) load_one(rs, c.sn2, is_v, buf, j);
+    for (int j = 0; j < Cfg::LOADS; ++j) load_one(rs, o, c.sn2, buf, j);
   };
 
   f32x16_t oacc[Cfg::DB];
@@ -265,13 +270,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
     __builtin_amdgcn_s_setprio(1);
     const lds_char *Kl = (const lds_char *)kbuf;
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
+    const uint32_t kof = lane_off(kc, false), vof = lane_off(vc, true);
     auto prefetch = [&](int ds) {
 #pragma unroll
       for (int li = ds * 2 * Cfg::LOADS / Cfg::DS; li < (ds + 1) * 2 * Cfg::LOADS / Cfg::DS; ++li) {
         if (li < Cfg::LOADS)
-          load_one(krs, kc.sn2, false, kdst, li);
+          load_one(krs, kof, kc.sn2, kdst, li);
         else
-          load_one(vrs, vc.sn2, true, vdst, li - Cfg::LOADS);
+          load_one(vrs, vof, vc.sn2, vdst, li - Cfg::LOADS);
       }
     };
     u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
@@ -361,6 +367,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
       for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(K0, ds, sa0, sa1);
     }
+    __syncthreads();  // every wave has read kbuf0 before step 0 loads K_2 into it
     // Steps alternate buffers: even steps read kbuf1 / vbuf0 and load K into kbuf0 / V into
     // vbuf1; odd steps the other way round.  Unrolled by two so the score registers swap roles
     // instead of being copied.
