@@ -50,7 +50,8 @@ static int history_lo(const fa_oracle_problem *p) {
  * reference key kframe carries the image index instead. */
 static int sees(const fa_oracle_problem *p, int qkind, int qframe, int kkind, int kframe) {
   if (qkind == FAO_TGT) {
-    if (kkind == FAO_TGT) return kframe >= history_lo(p) && kframe < p->cs + p->C;
+    if (kkind == FAO_TGT)
+      return (kframe >= history_lo(p) || kframe < p->sink) && kframe < p->cs + p->C;
     if (kkind == FAO_SRC) return kframe == qframe;
     return qframe >= p->ref_t0[kframe];
   }

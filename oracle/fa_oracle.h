@@ -17,6 +17,11 @@
  *    over target tokens becomes block-wise causal, conditioned on the valid
  *    historical states up to the current segment; the Vidu S2 structured
  *    summary (section 4.3) adds the sliding-window context.
+ *  - Sink frames: the tech report's Self-Replay Forcing paragraph and the
+ *    structured summary's S1/S2 section keep "sink blocks" beside the
+ *    sliding-window context without saying more; read here as: the first
+ *    `sink` frames of the stream stay visible to every later target row, on
+ *    top of the window (sink = 0: none).
  *  - Vidu S2 structured summary section 5.2: a source frame leaves the cache
  *    once its target frame is produced (so a chunk only reads its own source
  *    frames).
@@ -65,6 +70,7 @@ typedef struct {
   const float *k_hist, *v_hist;         /* target K/V of absolute frames hist_first .. cs+C-1 */
   const float *k_src, *v_src;           /* source K/V of frames cs .. cs+C-1 */
   const float *k_ref, *v_ref;           /* reference K/V */
+  int sink;         /* streaming: frames 0 .. sink-1 stay visible to target rows; 0 = none */
 } fa_oracle_problem;
 
 /* Number of threads OpenMP will use (for reporting). */

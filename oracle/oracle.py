@@ -85,6 +85,7 @@ class _CProblem(C.Structure):
         ("k_hist", C.c_void_p), ("v_hist", C.c_void_p),
         ("k_src", C.c_void_p), ("v_src", C.c_void_p),
         ("k_ref", C.c_void_p), ("v_ref", C.c_void_p),
+        ("sink", C.c_int),
     ]
 
 
@@ -100,7 +101,8 @@ class Problem:
     """One call's worth of inputs.  Arrays are [tokens, H, D] fp32.
 
     k_hist / v_hist hold target frames hist_first .. cs+C-1 by absolute frame
-    (the current chunk's own target K/V are its last C frames)."""
+    (the current chunk's own target K/V are its last C frames).  sink: frames
+    0 .. sink-1 stay visible to target rows beside the window (streaming)."""
     T: int
     C: int
     H: int
@@ -120,6 +122,7 @@ class Problem:
     v_src: Optional[np.ndarray] = None
     k_ref: Optional[np.ndarray] = None
     v_ref: Optional[np.ndarray] = None
+    sink: int = 0
     _keep: list = field(default_factory=list, repr=False)
 
     def rows(self, kind: int) -> int:
@@ -139,7 +142,7 @@ class Problem:
             arrs[name] = a.ctypes.data if a is not None and a.size else None
         self._keep = keep
         return _CProblem(self.T, self.C, self.cs, self.window, self.hist_first, n, rt, r0,
-                         self.H, self.D, float(scale), **arrs)
+                         self.H, self.D, float(scale), **arrs, sink=int(self.sink))
 
 
 def _fp(a):

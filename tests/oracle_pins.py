@@ -17,6 +17,8 @@ What pins what:
   permutation       key order inside a frame does not matter
   split / merge     LSE-weighted merge of two disjoint key sets
   streaming         cs = 0 streaming == bidirectional; window >= cs == all
+  sink              sink 0 == plain window; sink reaching the window == all history;
+                    exactly the sink and window frames matter
   smoothing         subtracting a per-channel vector from all keys is exact
   quantiser         hand-derived codes, round-trip bound, torch float8_e4m3fn
 """
@@ -37,7 +39,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 # ---------------------------------------------------------------------------- helpers
 
 def rand_problem(seed, T, C, H, D, cs=0, window=-1, hist_first=None, ref_tokens=(),
-                 ref_t0=(), bf16=False):
+                 ref_t0=(), bf16=False, sink=0):
     g = np.random.default_rng(seed)
     if hist_first is None:
         hist_first = 0
@@ -54,12 +56,12 @@ def rand_problem(seed, T, C, H, D, cs=0, window=-1, hist_first=None, ref_tokens=
                      ref_tokens=list(ref_tokens), ref_t0=list(ref_t0),
                      q_tgt=n(C * T, H, D), q_src=n(C * T, H, D), q_ref=n(R, H, D),
                      k_hist=n(nh, H, D), v_hist=n(nh, H, D), k_src=n(C * T, H, D),
-                     v_src=n(C * T, H, D), k_ref=n(R, H, D), v_ref=n(R, H, D))
+                     v_src=n(C * T, H, D), k_ref=n(R, H, D), v_ref=n(R, H, D), sink=sink)
 
 
 def clone(p, **kw):
     d = {k: getattr(p, k) for k in ("T", "C", "H", "D", "cs", "window", "hist_first",
-                                    "ref_tokens", "ref_t0", "scale")}
+                                    "ref_tokens", "ref_t0", "scale", "sink")}
     for k in ("q_tgt", "q_src", "q_ref", "k_hist", "v_hist", "k_src", "v_src", "k_ref", "v_ref"):
         a = getattr(p, k)
         d[k] = None if a is None else a.copy()
@@ -92,7 +94,7 @@ def dense_mask(p, qkind):
     ref_ok = (kk == REF)[None] & (qf[:, None] >= t0[None])
     if qkind == SRC:
         return same_src | ref_ok
-    tgt_ok = ((kk == TGT) & (kf >= lo) & (kf < p.cs + p.C))[None]
+    tgt_ok = ((kk == TGT) & ((kf >= lo) | (kf < p.sink)) & (kf < p.cs + p.C))[None]
     return tgt_ok | same_src | ref_ok
 
 
@@ -147,7 +149,7 @@ def pin_golden_masks(lib):
         meta, rows, want = read_golden(os.path.join(GOLDEN, fn))
         p0 = O.Problem(T=meta["T"], C=meta["C"], H=1, D=1, cs=meta["cs"], window=meta["window"],
                        hist_first=meta["hist_first"], ref_tokens=meta["ref_tokens"],
-                       ref_t0=meta["ref_t0"])
+                       ref_t0=meta["ref_t0"], sink=meta.get("sink", 0))
         nk = (p0.cs + p0.C - p0.hist_first) * p0.T * 1 + p0.C * p0.T + sum(p0.ref_tokens)
         D = max(nk, 2)
         eye = np.eye(nk, D, dtype=np.float32)[:, None, :]
@@ -160,7 +162,8 @@ def pin_golden_masks(lib):
         p = O.Problem(T=p0.T, C=p0.C, H=1, D=D, cs=p0.cs, window=p0.window,
                       hist_first=p0.hist_first, ref_tokens=p0.ref_tokens, ref_t0=p0.ref_t0,
                       q_tgt=z(ns), q_src=z(ns), q_ref=z(R), k_hist=k(nh), v_hist=eye[:nh],
-                      k_src=k(ns), v_src=eye[nh:nh + ns], k_ref=k(R), v_ref=eye[nh + ns:])
+                      k_src=k(ns), v_src=eye[nh:nh + ns], k_ref=k(R), v_ref=eye[nh + ns:],
+                      sink=p0.sink)
         res = O.attn(p, lib=lib)
         got = np.concatenate([res[TGT][0][:, 0, :nk], res[SRC][0][:, 0, :nk],
                               res[REF][0][:, 0, :nk]], 0) > 0
@@ -169,7 +172,7 @@ def pin_golden_masks(lib):
 
 
 LAYOUTS = [
-    # (T, C, cs, window, hist_first, ref_tokens, ref_t0)
+    # (T, C, cs, window, hist_first, ref_tokens, ref_t0[, sink])
     (1, 1, 0, -1, 0, (), ()),
     (7, 2, 0, -1, 0, (3,), (0,)),
     (7, 3, 0, -1, 0, (3, 5), (0, 2)),
@@ -180,12 +183,23 @@ LAYOUTS = [
     (4, 2, 3, 12, 0, (3,), (4,)),
     (4, 2, 9, 0, 9, (), ()),
     (2, 3, 6, -1, 0, (2,), (7,)),
+    (3, 2, 9, 3, 0, (2,), (10,), 2),
+    (2, 3, 12, 4, 0, (), (), 5),
+    (3, 2, 4, 1, 0, (2,), (0,), 9),
 ]
 
 
+def layout_args(lay):
+    T, C, cs, w, hf, rt, r0, *rest = lay
+    return dict(T=T, C=C, cs=cs, window=w, hist_first=hf, ref_tokens=rt, ref_t0=r0,
+                sink=rest[0] if rest else 0)
+
+
 def pin_bruteforce(lib):
-    for i, (T, C, cs, w, hf, rt, r0) in enumerate(LAYOUTS):
-        p = rand_problem(100 + i, T, C, 2, 8, cs, w, hf, rt, r0)
+    for i, lay in enumerate(LAYOUTS):
+        a = layout_args(lay)
+        p = rand_problem(100 + i, a["T"], a["C"], 2, 8, a["cs"], a["window"], a["hist_first"],
+                         a["ref_tokens"], a["ref_t0"], sink=a["sink"])
         res = O.attn(p, lib=lib)
         for kind in (TGT, SRC, REF):
             if p.rows(kind) == 0:
@@ -242,7 +256,8 @@ def expected_count(p, kind, row):
     if kind == SRC:
         return p.T + refs
     lo = 0 if p.window < 0 else max(0, p.cs - p.window)
-    return (p.cs + p.C - lo) * p.T + p.T + refs
+    sink_only = max(0, min(p.sink, lo))  # sink frames below the window
+    return (p.cs + p.C - lo + sink_only) * p.T + p.T + refs
 
 
 def visible_mean(p, kind, row, h):
@@ -253,6 +268,9 @@ def visible_mean(p, kind, row, h):
     parts = []
     if kind == TGT:
         lo = 0 if p.window < 0 else max(0, p.cs - p.window)
+        sink_end = min(p.sink, lo)
+        if sink_end > 0:
+            parts.append(p.v_hist[(0 - p.hist_first) * p.T:(sink_end - p.hist_first) * p.T, h])
         parts.append(p.v_hist[(lo - p.hist_first) * p.T:, h])
     parts.append(p.v_src[(f - p.cs) * p.T:(f - p.cs + 1) * p.T, h])
     off = 0
@@ -264,8 +282,10 @@ def visible_mean(p, kind, row, h):
 
 
 def pin_q_zero(lib):
-    for i, (T, C, cs, w, hf, rt, r0) in enumerate(LAYOUTS):
-        p = rand_problem(200 + i, T, C, 2, 8, cs, w, hf, rt, r0)
+    for i, lay in enumerate(LAYOUTS):
+        a = layout_args(lay)
+        p = rand_problem(200 + i, a["T"], a["C"], 2, 8, a["cs"], a["window"], a["hist_first"],
+                         a["ref_tokens"], a["ref_t0"], sink=a["sink"])
         for name in ("q_tgt", "q_src", "q_ref"):
             setattr(p, name, np.zeros_like(getattr(p, name)))
         res = O.attn(p, lib=lib)
@@ -406,6 +426,30 @@ def pin_streaming_consistency(lib):
     assert not np.array_equal(st[0], all_h[0]), "window < cs drops a frame"
 
 
+def pin_sink(lib):
+    """Sink frames (reading of the pages' sink blocks): frames 0 .. sink-1 stay visible beside
+    the window.  sink = 0 is the plain window; a sink that reaches the window is all history;
+    a frame neither in the sink nor in the window is invisible, a sink frame is visible."""
+    T, C = 3, 2
+    p = rand_problem(91, T, C, 2, 8, cs=8, window=3, hist_first=0, ref_tokens=(2,), ref_t0=(0,))
+    plain = O.attn(p, kinds=(TGT,), lib=lib)[TGT]
+    _eq(O.attn(clone(p, sink=0), kinds=(TGT,), lib=lib)[TGT][0], plain[0], "sink 0 = window")
+    all_h = O.attn(clone(p, window=-1), kinds=(TGT,), lib=lib)[TGT]
+    for sk in (5, 6, 10):  # [0, sk) u [5, 8) = all history
+        st = O.attn(clone(p, sink=sk), kinds=(TGT,), lib=lib)[TGT]
+        _eq(st[0], all_h[0], "sink reaching the window keeps all history (sink %d)" % sk)
+    q = clone(p, sink=2)
+    base = O.attn(q, kinds=(TGT,), lib=lib)[TGT]
+    assert not np.array_equal(base[0], plain[0]), "sink frames are visible"
+    g = np.random.default_rng(93)
+    for f, visible in ((0, True), (1, True), (2, False), (4, False), (5, True)):
+        r = clone(q)
+        r.k_hist[f * T:(f + 1) * T] = g.standard_normal((T, 2, 8)).astype(np.float32)
+        got = O.attn(r, kinds=(TGT,), lib=lib)[TGT]
+        same = np.array_equal(got[0], base[0])
+        assert same != visible, "frame %d visible=%s under sink 2, window 3" % (f, visible)
+
+
 def pin_smoothing(lib):
     T, C = 4, 3
     p = rand_problem(81, T, C, 2, 8, cs=3, window=2, ref_tokens=(3,), ref_t0=(0,), bf16=True)
@@ -489,4 +533,4 @@ def pin_kmean(lib):
 ALL_PINS = [pin_golden_masks, pin_bruteforce, pin_f1_full_attention, pin_two_keys,
             pin_large_scores, pin_q_zero,
             pin_ones_v, pin_perturbations, pin_permutation, pin_split_merge,
-            pin_streaming_consistency, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean]
+            pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean]

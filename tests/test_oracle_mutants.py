@@ -44,6 +44,10 @@ MUTANTS = {
     "e4m3 ties odd": ("(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
     "e4m3 bias 8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
                     "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "sink ignored": ("(kframe >= history_lo(p) || kframe < p->sink)",
+                     "(kframe >= history_lo(p))"),
+    "sink off by one": ("(kframe >= history_lo(p) || kframe < p->sink)",
+                        "(kframe >= history_lo(p) || kframe <= p->sink)"),
     "kmean off by one": ("mean[h * D + d] = n ? (float)(acc / (double)n) : 0.0f;",
                          "mean[h * D + d] = n ? (float)(acc / (double)(n + 1)) : 0.0f;"),
 }
