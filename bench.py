@@ -143,9 +143,11 @@ def run_stream_bench(args, torch, W, B):
     }
 
 
-def time_single_call(wid, torch, W, B, reps=10):
-    """One-shot workloads (bidirectional 21x1560, 3600-token chunk): attention call only."""
+def time_single_call(wid, torch, W, B, reps=10, sink=0):
+    """One-shot workloads (bidirectional 21x1560, 3600-token chunk, the steady chunk of the
+    1560-token stream with sink frames): attention call only."""
     w = W.WORKLOADS[wid]
+    name = w.name
     dev = lambda x: torch.from_numpy(x).unsqueeze(0).to("cuda").to(torch.bfloat16).contiguous()
     if wid == 1:
         x = W.chunk_tensors(w, 0, with_queries_src_ref=True)
@@ -156,17 +158,20 @@ def time_single_call(wid, torch, W, B, reps=10):
         rows = {"tgt": w.C * w.T, "src": w.C * w.T, "ref": sum(w.ref_tokens)}
         L = B.fa_layout_build(d)
     else:
-        cs = w.first_cs
+        cs = w.first_cs if wid == 3 else (w.chunks - 1) * w.C
+        cap = w.cache_frames + sink  # sink frames take slots of their own
         x = W.chunk_tensors(w, cs // w.C)
         r = W.ref_tensors(w)
         t = {n: dev(v) for n, v in {**x, **r}.items()}
         for n in ("k_ring", "v_ring"):
-            t[n] = torch.randn((1, w.cache_frames * w.T, w.H, w.D), device="cuda").to(torch.bfloat16)
+            t[n] = torch.randn((1, cap * w.T, w.H, w.D), device="cuda").to(torch.bfloat16)
         d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.t0_for(cs),
-                        chunk_start=cs, window=w.window, cache_frames=w.cache_frames,
-                        query_rows=1, dtype=B.FA_BF16)
+                        chunk_start=cs, window=w.window, cache_frames=cap,
+                        query_rows=1, dtype=B.FA_BF16, sink_frames=sink)
         rows = {"tgt": w.C * w.T}
         L = B.fa_layout_build(d, cs - w.window)
+        if sink:
+            name = "%s + %d sink frames (steady chunk, cs=%d)" % (w.name, sink, cs)
     for nm, n in rows.items():
         t["o_" + nm] = torch.empty((1, n, w.H, w.D), dtype=torch.bfloat16, device="cuda")
         t["lse_" + nm] = torch.empty((1, w.H, n), dtype=torch.float32, device="cuda")
@@ -184,7 +189,7 @@ def time_single_call(wid, torch, W, B, reps=10):
     ms = [e[0].elapsed_time(e[1]) for e in ev]
     fl = B.fa_layout_stats(L)["useful_flops"]
     med = statistics.median(ms)
-    return {"workload": w.name, "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+    return {"workload": name, "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
             "useful_tflops": round(fl / med / 1e9, 2),
             "mfma_frac": round(fl / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
@@ -433,7 +438,8 @@ def main():
     if not args.no_extra:
         log("bench: other bf16 workloads")
         out["other_workloads"] = [time_single_call(1, torch, W, B), time_single_call(3, torch, W, B),
-                                  time_lowbit_chunk(torch, W, B)]
+                                  time_lowbit_chunk(torch, W, B),
+                                  time_single_call(2, torch, W, B, sink=3)]
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)

@@ -134,9 +134,15 @@ static fa_status ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
   if (d->tokens_per_frame < 1 || d->heads < 1 || d->batch < 1)
     return fail(FA_ERR_INVALID, "bad geometry");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim");
-  if (frames < 0 || frames > d->cache_frames)
-    return fail(FA_ERR_INVALID, "frames must be in [0, cache_frames]");
+  if (d->sink_frames < 0 || d->sink_frames > d->cache_frames)
+    return fail(FA_ERR_INVALID, "sink_frames must be in [0, cache_frames]");
   if (first_frame < 0) return fail(FA_ERR_INVALID, "first_frame must be >= 0");
+  if (frames < 0) return fail(FA_ERR_INVALID, "frames must be >= 0");
+  // non-sink frames of this append cycle through cache_frames - sink_frames slots
+  const int64_t nonsink =
+      (int64_t)first_frame + frames - std::max<int64_t>(first_frame, d->sink_frames);
+  if (nonsink > (int64_t)d->cache_frames - d->sink_frames)
+    return fail(FA_ERR_INVALID, "more non-sink frames than the ring's cycling slots");
   if (frames == 0) return FA_OK;
   const int es = d->dtype == FA_F32 ? 4 : 2;
   const fa_tensor *t[4] = {k_ring, v_ring, k_chunk, v_chunk};
@@ -159,6 +165,7 @@ static fa_status ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
   a.frames = frames;
   a.first_frame = first_frame;
   a.cache_frames = d->cache_frames;
+  a.sink = d->sink_frames;
   a.chunks16 = d->head_dim * es / 16;
   a.batch = d->batch;
   hipError_t e = launch_ring_append(a, stream);
@@ -383,7 +390,8 @@ extern "C" fa_status fa_stream_advance(fa_stream *s, const fa_io *io, fa_hip_str
                              s->next_frame, s->d.frames, (hipStream_t)stream);
   if (st != FA_OK) return st;
   s->next_frame += s->d.frames;
-  s->ring_first = std::max(s->ring_first, s->next_frame - s->d.cache_frames);
+  // the cycling part holds the last cache_frames - sink_frames frames; sink frames stay
+  s->ring_first = std::max(s->ring_first, s->next_frame - (s->d.cache_frames - s->d.sink_frames));
   s->current = nullptr;
   return FA_OK;
 }
@@ -412,8 +420,10 @@ extern "C" fa_status fa_stream_state(const fa_stream *s, int32_t *next_frame,
 
 extern "C" fa_status fa_stream_seek(fa_stream *s, int32_t next_frame, int32_t ring_first_frame) {
   if (!s) return fail(FA_ERR_INVALID, "stream is NULL");
+  const int32_t S = s->d.sink_frames;
   if (next_frame < 0 || ring_first_frame < 0 || ring_first_frame > next_frame ||
-      next_frame - ring_first_frame > s->d.cache_frames)
+      (next_frame > S &&
+       next_frame - std::max(ring_first_frame, S) > s->d.cache_frames - S))
     return fail(FA_ERR_INVALID, "inconsistent stream state");
   s->next_frame = next_frame;
   s->ring_first = ring_first_frame;

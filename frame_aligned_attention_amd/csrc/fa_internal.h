@@ -79,7 +79,14 @@ struct RingArgs {
   int64_t dsb[2], dsn[2], dsh[2];
   int32_t T, H, frames, first_frame, cache_frames, chunks16;  // 16-byte chunks per (token, head)
   int32_t batch;
+  int32_t sink;  // sink frames: slots 0 .. sink-1 for good
 };
+
+// Ring slot of absolute frame g: a sink frame keeps its own slot, the others cycle through the
+// cache_frames - sink remaining slots (callers make sure there is one when g >= sink).
+__host__ __device__ inline int ring_slot(int g, int sink, int cache_frames) {
+  return g < sink ? g : sink + (g - sink) % (cache_frames - sink);
+}
 
 // Launchers (defined in the .hip files); return hipError_t of the launch.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int grid, hipStream_t s);

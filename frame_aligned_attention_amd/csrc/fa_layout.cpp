@@ -4,8 +4,9 @@
 // paragraphs on frame-aligned attention and on causal streaming editing;
 // structured summary sections 4.3 and 5.2; news clipping point 7): a target
 // row of frame f reads the target keys of the call's frames (plus, when
-// streaming, the `window` history frames before the chunk), the source keys
-// of frame f, and reference image r iff f >= t0[r].  Here that rule is
+// streaming, the `window` history frames before the chunk and the stream's
+// first sink_frames frames), the source keys of frame f, and reference image
+// r iff f >= t0[r].  Here that rule is
 // turned, once per descriptor, into per-tile key ranges so that the kernels
 // never build a dense mask and never touch keys outside the ranges.
 #include <algorithm>
@@ -32,6 +33,7 @@ static fa_status validate(const fa_layout_desc *d, int32_t ring_first, int32_t *
   if (d->chunk_start < 0) return fail(FA_ERR_INVALID, "chunk_start must be >= 0");
   if (d->window < FA_WINDOW_ALL) return fail(FA_ERR_INVALID, "window must be >= -1");
   if (d->cache_frames < 0) return fail(FA_ERR_INVALID, "cache_frames must be >= 0");
+  if (d->sink_frames < 0) return fail(FA_ERR_INVALID, "sink_frames must be >= 0");
   if (d->query_rows <= 0 || d->query_rows > 7)
     return fail(FA_ERR_INVALID, "query_rows must be a non-empty set of FA_Q_* bits");
   if (d->batch < 1 || d->heads < 1) return fail(FA_ERR_INVALID, "batch and heads must be >= 1");
@@ -54,13 +56,19 @@ static fa_status validate(const fa_layout_desc *d, int32_t ring_first, int32_t *
   const int64_t lo = d->window < 0 ? 0 : std::max<int64_t>(0, cs - d->window);
   if (cs + d->frames >= lim) return fail(FA_ERR_UNSUPPORTED, "chunk_start too large");
   if (ring_first > cs) return fail(FA_ERR_INVALID, "ring_first_frame is after chunk_start");
-  if (lo < cs) {  // some history is visible
-    if (d->cache_frames < cs - lo)
+  // Visible history: the sink frames before the chunk, [0, min(S, cs)), in slots of their own,
+  // and the window [lo, cs); its non-sink part [nlo, cs) cycles through cap - S slots.
+  const int64_t S = d->sink_frames, cap = d->cache_frames;
+  const int64_t nlo = std::max(lo, S);
+  if (std::min(S, cs) > 0 && cap < S)
+    return fail(FA_ERR_CAPACITY, "the ring has fewer slots than sink frames");
+  if (nlo < cs) {  // some non-sink history is visible
+    if (cap - S < cs - nlo)
       return fail(FA_ERR_CAPACITY, "the ring holds fewer frames than the visible history");
-    if (ring_first < 0) ring_first = (int32_t)lo;
-    if (ring_first > lo)
+    if (ring_first < 0) ring_first = (int32_t)nlo;
+    if (ring_first > nlo)
       return fail(FA_ERR_CAPACITY, "visible history is older than the ring's oldest frame");
-    if (ring_first < cs - d->cache_frames)
+    if (std::max<int64_t>(ring_first, S) < cs - (cap - S))
       return fail(FA_ERR_INVALID, "ring_first_frame is older than the ring can hold");
   } else {
     if (ring_first < 0) ring_first = (int32_t)cs;
@@ -116,13 +124,18 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   L->q_rows[1] = (d.query_rows & FA_Q_SOURCE) ? F * T : 0;
   L->q_rows[2] = (d.query_rows & FA_Q_REF) ? ref_total : 0;
 
-  // Ring runs: slots of the visible history frames [hist_lo, cs), as maximal runs in slot order
-  // (the softmax does not care about key order).
+  // Ring runs: slots of the visible history frames (the sink frames before the chunk and the
+  // window [hist_lo, cs)), as maximal runs in slot order (the softmax does not care about key
+  // order).
+  const int S = d.sink_frames;
+  const int hist_frames = (cs - hist_lo) + std::min(S, hist_lo);
+  L->hist_frames = hist_frames;
   std::vector<DevRange> ring_runs;
-  if (hist_lo < cs) {
+  if (hist_frames > 0) {
     const int cap = d.cache_frames;
     std::vector<char> used(cap, 0);
-    for (int g = hist_lo; g < cs; ++g) used[g % cap] = 1;
+    for (int g = 0; g < cs; ++g)
+      if (g >= hist_lo || g < S) used[ring_slot(g, S, cap)] = 1;
     for (int s = 0; s < cap;) {
       if (!used[s]) { ++s; continue; }
       int e = s;
@@ -166,7 +179,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
     if (!L->q_rows[kind]) continue;
     for (int f = 0; f < F; ++f) {
       double keys = T;  // own-frame source
-      if (kind == 0) keys += (double)(cs + F - hist_lo) * T;
+      if (kind == 0) keys += (double)(F + hist_frames) * T;
       for (int r = 0; r < d.n_ref; ++r)
         if (cs + f >= d.ref_t0[r]) keys += d.ref_tokens[r];
       useful += keys * T;
@@ -189,7 +202,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   bool seg_used[4] = {false, false, false, false};
   double seg_keys[4] = {0, 0, 0, 0};
   for (const DevRange &r : L->ranges) seg_used[r.seg] = true;
-  seg_keys[FA_SEG_RING] = (double)(cs - hist_lo) * T;
+  seg_keys[FA_SEG_RING] = (double)hist_frames * T;
   seg_keys[FA_SEG_TGT] = (double)F * T;
   seg_keys[FA_SEG_SRC] = (double)F * T;
   seg_keys[FA_SEG_REF] = ref_total;

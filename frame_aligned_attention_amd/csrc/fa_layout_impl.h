@@ -24,7 +24,8 @@ struct DeviceMap {
 struct fa_layout {
   fa_layout_desc d;
   int32_t ring_first = 0;   // oldest frame the ring holds (resolved)
-  int32_t hist_lo = 0;      // first visible history frame
+  int32_t hist_lo = 0;      // first frame of the visible window
+  int32_t hist_frames = 0;  // visible history frames (window and sink frames before the chunk)
   int32_t block_m = 0, block_n = 0;
   int32_t q_rows[3] = {0, 0, 0};
   int32_t ref_total = 0;

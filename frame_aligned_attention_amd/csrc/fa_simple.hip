@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(256) ring_append_kernel(const RingArgs a) {
     const int b = (int)(r % a.batch); r /= a.batch;
     const int i = (int)r;  // 0: K, 1: V
     const int fi = tok / a.T, t = tok - fi * a.T;
-    const int slot = (a.first_frame + fi) % a.cache_frames;
+    const int slot = ring_slot(a.first_frame + fi, a.sink, a.cache_frames);
     const char *src = (const char *)a.src[i] + b * a.ssb[i] + tok * a.ssn[i] + h * a.ssh[i] + c * 16;
     char *dst = (char *)a.dst[i] + b * a.dsb[i] + ((int64_t)slot * a.T + t) * a.dsn[i] +
                 h * a.dsh[i] + c * 16;

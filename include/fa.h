@@ -73,6 +73,11 @@ enum { FA_Q_TARGET = 1, FA_Q_SOURCE = 2, FA_Q_REF = 4 };
  * chunk_start = absolute frame of the chunk's first frame, window = history
  * frames kept visible before it (block-wise causal: every row of the chunk
  * sees the same history), cache_frames = ring capacity in frames.
+ * sink_frames: the first frames of the stream that stay visible to every
+ * later chunk beside the window (the sink blocks the tech report's
+ * Self-Replay Forcing paragraph and the structured summary's S1/S2 section
+ * keep next to the sliding window; how many is the caller's choice).  They
+ * occupy ring slots 0 .. sink_frames-1 for good.
  */
 typedef struct {
   int32_t frames;           /* query frames in the call (F or C), >= 1 */
@@ -87,6 +92,7 @@ typedef struct {
   int32_t batch, heads, head_dim; /* head_dim 64 or 128; query heads == key heads */
   int32_t dtype;            /* fa_dtype */
   float scale;              /* softmax scale; 0 = 1/sqrt(head_dim) */
+  int32_t sink_frames;      /* streaming: frames 0 .. sink_frames-1 stay visible; 0 = none */
 } fa_layout_desc;
 
 /* A device tensor [batch][tokens][heads][head_dim], head_dim contiguous. */
@@ -101,7 +107,9 @@ typedef struct {
  * frames*T, q_ref/o_ref sum(ref_tokens).  Keys: k/v_tgt are the call's own
  * target frames (frames*T), k/v_src the same frames' source (frames*T),
  * k/v_ref the references, k/v_ring the ring (cache_frames*T; absolute frame
- * g lives in slot g mod cache_frames, tokens [slot*T, slot*T+T)).
+ * g lives in slot g if g < sink_frames, else in slot
+ * sink_frames + (g - sink_frames) mod (cache_frames - sink_frames); tokens
+ * [slot*T, slot*T+T)).  With sink_frames = 0: slot g mod cache_frames.
  * lse_*: [batch][heads][rows] fp32, NULL to skip.  Outputs of kinds not in
  * query_rows may be absent.
  */
@@ -130,9 +138,11 @@ const char *fa_last_error(void);
  * range are never read.  The work order (longest tiles first, heads grouped
  * per XCD) is fixed here.  Pure host work; the block map goes to the device
  * on first use.
- * ring_first_frame: oldest absolute frame the ring holds, or -1 for "all of
- * [max(0, chunk_start - window), chunk_start)".  Visible history older than
- * it returns FA_ERR_CAPACITY.
+ * ring_first_frame: the ring holds every frame of [ring_first_frame,
+ * chunk_start) and every sink frame before chunk_start; -1 = "everything
+ * visible is held".  Visible history older than it (sink frames aside)
+ * returns FA_ERR_CAPACITY, as does a ring too small for the visible history
+ * (cache_frames - sink_frames cycling slots) or for the sink frames.
  * *out receives a new layout owned by the caller (fa_layout_destroy).
  */
 fa_status fa_layout_build(const fa_layout_desc *d, int32_t ring_first_frame, fa_layout **out);
@@ -211,8 +221,10 @@ fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *o
  * Streaming append (structured summary section 4.3, sliding-window KV cache;
  * section 5.2, source frames are not cached): copies frames [0, frames) of
  * k_chunk/v_chunk -- absolute frames first_frame .. first_frame+frames-1 --
- * into ring slots (frame mod d->cache_frames).  Element type from d->dtype
- * (FA_LOWBIT rings hold bf16 and are quantised per call).  Asynchronous.
+ * into their ring slots (see fa_io; sink frames keep slots 0 ..
+ * sink_frames-1).  At most cache_frames - sink_frames non-sink frames per
+ * call, else FA_ERR_INVALID.  Element type from d->dtype (FA_LOWBIT rings
+ * hold bf16 and are quantised per call).  Asynchronous.
  */
 fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const fa_tensor *v_ring,
                          const fa_tensor *k_chunk, const fa_tensor *v_chunk, int32_t first_frame,
@@ -237,8 +249,9 @@ fa_status fa_stream_chunk(fa_stream *s, const fa_io *io, fa_hip_stream stream);
 fa_status fa_stream_advance(fa_stream *s, const fa_io *io, fa_hip_stream stream);
 /* The layout the next chunk will use (owned by the stream; valid until destroy). */
 fa_status fa_stream_layout(fa_stream *s, const fa_layout **out);
-/* next_frame: chunk_start of the next chunk; ring_first_frame: oldest frame held
- * (== next_frame when the ring is empty). */
+/* next_frame: chunk_start of the next chunk; ring_first_frame: the ring holds
+ * [ring_first_frame, next_frame) and the sink frames (== next_frame when it
+ * holds nothing else). */
 fa_status fa_stream_state(const fa_stream *s, int32_t *next_frame, int32_t *ring_first_frame);
 /* Resume at a saved state (the ring tensors must hold what that state says). */
 fa_status fa_stream_seek(fa_stream *s, int32_t next_frame, int32_t ring_first_frame);

@@ -88,6 +88,7 @@ class Call:
     v_src: Optional[np.ndarray] = None
     k_ref: Optional[np.ndarray] = None
     v_ref: Optional[np.ndarray] = None
+    sink: int = 0  # frames 0 .. sink-1 stay visible (streaming)
 
     @property
     def fa_dtype(self):
@@ -97,7 +98,7 @@ class Call:
         return B.make_desc(self.C, self.T, self.H, self.D, ref_tokens=self.ref_tokens,
                            ref_t0=self.ref_t0, chunk_start=self.cs, window=self.window,
                            cache_frames=self.cache, query_rows=self.query_rows,
-                           dtype=self.fa_dtype)
+                           dtype=self.fa_dtype, sink_frames=self.sink)
 
     def problem(self) -> O.Problem:
         z = np.zeros((0, self.H, self.D), np.float32)
@@ -107,14 +108,14 @@ class Call:
                          q_tgt=self.q.get(TGT, z), q_src=self.q.get(SRC, z), q_ref=self.q.get(REF, z),
                          k_hist=self.k_hist, v_hist=self.v_hist, k_src=self.k_src,
                          v_src=self.v_src, k_ref=self.k_ref if self.k_ref is not None else z,
-                         v_ref=self.v_ref if self.v_ref is not None else z)
+                         v_ref=self.v_ref if self.v_ref is not None else z, sink=self.sink)
 
     def kinds(self):
         return [k for k, bit in ((TGT, 1), (SRC, 2), (REF, 4)) if self.query_rows & bit]
 
 
 def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tokens=(),
-                ref_t0=(), query_rows=7, scale_k=1.0) -> Call:
+                ref_t0=(), query_rows=7, scale_k=1.0, sink=0) -> Call:
     """Seeded N(0,1) inputs (bf16-rounded unless fp32) for one call."""
     g = np.random.default_rng(seed)
 
@@ -126,7 +127,7 @@ def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tok
     lo = 0 if window < 0 else max(0, cs - window)
     c = Call(T=T, C=C, H=H, D=D, dtype=dtype, cs=cs, window=window, cache=cache,
              ref_tokens=list(ref_tokens), ref_t0=list(ref_t0), query_rows=query_rows,
-             hist_first=lo if cache else 0)
+             hist_first=(0 if sink else lo) if cache else 0, sink=sink)
     c.q = {TGT: n(C * T, H, D), SRC: n(C * T, H, D), REF: n(R, H, D)}
     nh = (cs + C - c.hist_first) * T
     c.k_hist, c.v_hist = n(nh, H, D) * scale_k, n(nh, H, D)
@@ -135,15 +136,21 @@ def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tok
     return c
 
 
+def ring_slot(g, sink, cap):
+    """The ring layout fa.h documents: sink frames keep slots 0 .. sink-1, the others cycle."""
+    return g if g < sink else sink + (g - sink) % (cap - sink)
+
+
 def ring_tensors(c: Call, tdtype, poison=None):
-    """Ring buffers [1, cap*T, H, D] holding frames hist_first .. cs-1 in slot g % cap.
-    Slots not holding a visible frame are filled with `poison` (None = zeros)."""
+    """Ring buffers [1, cap*T, H, D] after appending frames hist_first .. cs-1 in order (each
+    to its ring slot, later frames overwriting earlier ones).  Slots never written are filled
+    with `poison` (None = zeros)."""
     cap, T = c.cache, c.T
     fill = 0.0 if poison is None else poison
     kr = np.full((cap * T, c.H, c.D), fill, np.float32)
     vr = np.full((cap * T, c.H, c.D), fill, np.float32)
     for g in range(c.hist_first, c.cs):
-        s = g % cap
+        s = ring_slot(g, c.sink, cap)
         i = (g - c.hist_first) * T
         kr[s * T:(s + 1) * T] = c.k_hist[i:i + T]
         vr[s * T:(s + 1) * T] = c.v_hist[i:i + T]

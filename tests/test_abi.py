@@ -80,6 +80,12 @@ def build_status(d, ring_first=-1):
     (dict(window=3, cache_frames=2), B.FA_ERR_CAPACITY),        # ring smaller than window
     (dict(window=-1, cache_frames=4), B.FA_ERR_CAPACITY),       # all history, 6 frames > 4
     (dict(tokens_per_frame=1 << 29, frames=2), B.FA_ERR_UNSUPPORTED),
+    (dict(sink_frames=-1), B.FA_ERR_INVALID),
+    (dict(sink_frames=2, cache_frames=5), B.FA_OK),              # 2 sink slots + 3 for the window
+    (dict(sink_frames=2, cache_frames=4), B.FA_ERR_CAPACITY),    # 2 cycling slots < window 3
+    (dict(sink_frames=5, window=0, cache_frames=4), B.FA_ERR_CAPACITY),  # 5 sink frames, 4 slots
+    (dict(sink_frames=6, window=0, cache_frames=6), B.FA_OK),    # history = the 6 sink frames
+    (dict(sink_frames=4, window=3, cache_frames=6), B.FA_OK),    # sink reaches the window
     (dict(), B.FA_OK),
     (dict(window=0, cache_frames=0), B.FA_OK),
     (dict(chunk_start=0, window=-1, cache_frames=0), B.FA_OK),  # no history at all
@@ -104,6 +110,14 @@ def test_ring_first_frame_checks():
     assert build_status(d, 4) == B.FA_ERR_CAPACITY  # frame 3 missing
     assert build_status(d, 1) == B.FA_ERR_INVALID   # 1..5 is 5 frames > capacity 4
     assert build_status(d, 7) == B.FA_ERR_INVALID   # after chunk_start
+
+
+def test_ring_first_frame_checks_with_sink():
+    d = desc(sink_frames=1, cache_frames=5)  # cs 6, window 3: sink 0 + frames 3, 4, 5
+    assert build_status(d, 3) == B.FA_OK
+    assert build_status(d, 2) == B.FA_OK          # cycling slots hold 2..5 (4 slots)
+    assert build_status(d, 4) == B.FA_ERR_CAPACITY  # frame 3 missing
+    assert build_status(d, 1) == B.FA_ERR_INVALID   # 1..5 is 5 frames > 4 cycling slots
 
 
 def test_last_error_is_set():
@@ -145,6 +159,12 @@ def test_ring_append_rejects_bad_args_on_host():
                                 1, None) == B.FA_ERR_INVALID
     assert B.lib.fa_ring_append(C.byref(d), C.byref(t), C.byref(t), C.byref(t), C.byref(t), 0, 0,
                                 None) == B.FA_OK  # nothing to do
+    d = desc(sink_frames=2)  # 2 sink slots, 2 cycling slots
+    assert B.lib.fa_ring_append(C.byref(d), C.byref(t), C.byref(t), C.byref(t), C.byref(t), 4, 3,
+                                None) == B.FA_ERR_INVALID  # 3 non-sink frames > 2 cycling slots
+    d = desc(sink_frames=5)  # more sink frames than slots
+    assert B.lib.fa_ring_append(C.byref(d), C.byref(t), C.byref(t), C.byref(t), C.byref(t), 0, 0,
+                                None) == B.FA_ERR_INVALID
 
 
 def test_stream_state_and_seek():
@@ -157,6 +177,11 @@ def test_stream_state_and_seek():
         s.seek(12, 13)
     with pytest.raises(B.FaError):
         s.seek(30, 3)  # 27 frames cannot be in a 12-frame ring
+    s2 = B.Stream(desc(chunk_start=0, window=4, cache_frames=7, sink_frames=2))
+    s2.seek(20, 15)  # sink 0, 1 and frames 15..19 in the 5 cycling slots
+    assert s2.state() == (20, 15)
+    with pytest.raises(B.FaError):
+        s2.seek(20, 14)  # 6 non-sink frames > 5 cycling slots
     s.set_refs([16, 8], [0, 14])
     with pytest.raises(B.FaError):
         s.set_refs([1] * 9, [0] * 9)

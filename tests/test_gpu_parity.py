@@ -68,15 +68,20 @@ STREAMS = [
     (14, 33, 2, 1, 64, 3, 12, 12, [5], [40]),        # warm-up, reference not yet visible
     (15, 17, 3, 2, 128, 6, -1, 9, [4], [0]),         # all history
     (16, 100, 3, 2, 128, 3, 0, 4, [200], [0]),       # window 0
+    # sink frames (last field): frames 0 .. sink-1 stay visible in slots of their own
+    (17, 50, 3, 2, 128, 12, 4, 7, [20], [0], 2),     # sink 0, 1 + window 8..11
+    (18, 40, 2, 2, 128, 15, 4, 6, [8], [5], 1),      # cycling part wraps
+    (19, 64, 3, 1, 128, 10, 0, 3, [16], [0], 2),     # window 0: the sink frames only
+    (20, 33, 2, 1, 64, 9, 3, 6, [5], [0], 3),        # head_dim 64
 ]
 
 
 @pytest.mark.parametrize("case", STREAMS, ids=["st%d" % c[0] for c in STREAMS])
 def test_streaming_calls(case):
-    seed, T, C, H, D, cs, win, cap, refs, t0s = case
+    seed, T, C, H, D, cs, win, cap, refs, t0s, *rest = case
     G.say("case: streaming %s" % (case,))
     c = G.random_call(seed, T, C, H, D, "bf16", cs=cs, window=win, cache=cap, ref_tokens=refs,
-                      ref_t0=t0s, query_rows=3)
+                      ref_t0=t0s, query_rows=3, sink=rest[0] if rest else 0)
     G.compare_all(c, G.run_call(c), "stream st%d" % seed)
 
 

@@ -18,13 +18,17 @@ TGT = G.TGT
 class StreamRun:
     """Drives fa_stream over seeded chunks of workload `wid` with `H` heads."""
 
-    def __init__(self, wid, H):
+    def __init__(self, wid, H, window=None, cache_frames=None, sink=0):
         self.w = W.WORKLOADS[wid]
+        if window is not None:
+            self.w = W.Workload(**{**self.w.__dict__, "window": window,
+                                   "cache_frames": cache_frames})
         w = self.w
         self.H = H
+        self.sink = sink
         self.desc = B.make_desc(w.C, w.T, H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
                                 chunk_start=0, window=w.window, cache_frames=w.cache_frames,
-                                query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16)
+                                query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16, sink_frames=sink)
         self.s = B.Stream(self.desc)
         z = lambda: torch.zeros((1, w.cache_frames * w.T, H, w.D), dtype=torch.bfloat16,
                                 device="cuda")
@@ -56,11 +60,11 @@ class StreamRun:
     def oracle_call(self, ch, x, ref_t0=None):
         w = self.w
         cs = ch * w.C
-        lo = max(0, cs - w.window)
+        lo = 0 if self.sink else max(0, cs - w.window)  # sink frames need the whole history
         c = G.Call(T=w.T, C=w.C, H=self.H, D=w.D, dtype="bf16", cs=cs, window=w.window,
                    cache=w.cache_frames, ref_tokens=list(w.ref_tokens),
                    ref_t0=list(ref_t0 if ref_t0 is not None else w.ref_t0), query_rows=1,
-                   hist_first=lo)
+                   hist_first=lo, sink=self.sink)
         kh = np.concatenate(self.k_all[lo // w.C:])
         vh = np.concatenate(self.v_all[lo // w.C:])
         off = (lo - (lo // w.C) * w.C) * w.T
@@ -133,3 +137,24 @@ def test_stream_reference_injected_mid_stream():
         if ch >= 2:
             c = run.oracle_call(ch, x)
             G.compare_sampled(c, {TGT: (o, lse)}, n_rows=40, what="inject chunk %d" % ch)
+
+
+def test_stream_with_sink_frames():
+    G.say("case: 12-chunk stream, T=1560, C=3, 2 sink frames + window 6 in an 8-frame ring, H=1")
+    run = StreamRun(2, H=1, window=6, cache_frames=8, sink=2)
+    w = run.w
+    for ch in range(12):
+        x, o, lse = run.run_chunk(ch)
+        c = run.oracle_call(ch, x)
+        if ch == 11:
+            ref = O.attn(c.problem(), kinds=(TGT,))[TGT]
+            G.tol_check(o, ref[0], "bf16", "chunk %d all rows" % ch, lse, ref[1])
+        else:
+            G.compare_sampled(c, {TGT: (o, lse)}, n_rows=24, what="sink chunk %d" % ch)
+    # sink frames 0, 1 in slots 0, 1; frames 30..35 in the cycling slots 2 + (f - 2) % 6
+    kr = G.host(run.k_ring)[0]
+    for f in (0, 1) + tuple(range(30, 36)):
+        s = G.ring_slot(f, 2, 8)
+        want = run.k_all[f // 3][(f % 3) * w.T:(f % 3 + 1) * w.T]
+        assert np.array_equal(kr[s * w.T:(s + 1) * w.T], want), f
+    assert run.s.state() == (36, 30)

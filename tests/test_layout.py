@@ -17,13 +17,20 @@ from oracle import oracle as O
 TGT, SRC, REF = O.FAO_TGT, O.FAO_SRC, O.FAO_REF
 
 
+def ring_slot(g, sink, cap):
+    """The ring layout fa.h documents: sink frames keep slots 0 .. sink-1, the others cycle."""
+    return g if g < sink else sink + (g - sink) % (cap - sink)
+
+
 def blockmap_columns(L, d, ring_first, ref_total):
     """{kind: list over rows of the visited key columns} in the oracle's key order
     (target frames 0 .. cs+C-1, then source frames, then reference tokens)."""
-    T, C, cs, cap = d.tokens_per_frame, d.frames, d.chunk_start, d.cache_frames
+    T, C, cs, cap, S = d.tokens_per_frame, d.frames, d.chunk_start, d.cache_frames, d.sink_frames
     nhist = (cs + C) * T
     nsrc = C * T
-    held = {g % cap: g for g in range(ring_first, cs)} if cap else {}
+    present = sorted(set(range(ring_first, cs)) | set(range(min(S, cs))))
+    held = {ring_slot(g, S, cap): g for g in present} if cap else {}
+    assert len(held) == len(present), "two held frames share a slot"
     n, bm, bn = B.fa_layout_tiles(L)
     out = {}
     for i in range(n):
@@ -64,7 +71,7 @@ def oracle_visibility(d, refs, t0s):
     p = O.Problem(T=T, C=C, H=1, D=nk, cs=cs, window=d.window, hist_first=0, ref_tokens=refs,
                   ref_t0=t0s, q_tgt=z(ns), q_src=z(ns), q_ref=z(R), k_hist=k(nh),
                   v_hist=eye[:nh], k_src=k(ns), v_src=eye[nh:nh + ns], k_ref=k(R),
-                  v_ref=eye[nh + ns:])
+                  v_ref=eye[nh + ns:], sink=d.sink_frames)
     res = O.attn(p)
     return {kind: res[kind][0][:, 0, :] > 0 for kind in res}
 
@@ -84,18 +91,27 @@ SMALL = [
     (3, 17, [4], [0], 6, -1, 8, 0, 3, B.FA_BF16),      # all history
     (2, 130, [9], [1], 0, 0, 0, -1, 7, B.FA_BF16),     # tiles across frame boundaries
     (3, 60, [200], [0], 3, 0, 4, -1, 7, B.FA_BF16),    # window 0: no history; 3 frames a tile
+    # sink frames (last field): slots 0 .. sink-1 for good, the rest cycle
+    (3, 50, [20], [0], 12, 4, 7, -1, 1, B.FA_BF16, 2),  # sink 0,1 + window 8..11 in slots 3..6
+    (3, 40, [8], [5], 15, 4, 6, -1, 3, B.FA_BF16, 1),   # window 11..14 wraps in slots 1..5
+    (2, 30, [], [], 4, 3, 5, -1, 1, B.FA_BF16, 3),      # sink overlaps the window: all history
+    (3, 20, [5], [0], 3, 2, 6, -1, 7, B.FA_F32, 5),     # sink beyond the chunk start
+    (2, 64, [16], [0], 10, 0, 3, -1, 1, B.FA_BF16, 2),  # window 0: only the sink frames
+    (3, 30, [10], [0], 14, 4, 7, 9, 1, B.FA_LOWBIT, 2), # ring_first given
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[str(i) for i in range(len(SMALL))])
 def test_blockmap_equals_oracle_visibility(case):
-    F, T, refs, t0s, cs, win, cap, rf, qr, dt = case
+    F, T, refs, t0s, cs, win, cap, rf, qr, dt, *rest = case
+    sink = rest[0] if rest else 0
     hd = 128
     d = B.make_desc(F, T, 1, hd, ref_tokens=refs, ref_t0=t0s, chunk_start=cs, window=win,
-                    cache_frames=cap, query_rows=qr, dtype=dt)
+                    cache_frames=cap, query_rows=qr, dtype=dt, sink_frames=sink)
     L = B.fa_layout_build(d, rf)
     lo = 0 if win < 0 else max(0, cs - win)
-    ring_first = rf if rf >= 0 else (lo if lo < cs else cs)
+    nlo = max(lo, sink)  # first visible non-sink history frame
+    ring_first = rf if rf >= 0 else (nlo if nlo < cs else cs)
     cols = blockmap_columns(L, d, ring_first, sum(refs))
     vis = oracle_visibility(d, refs, t0s)
     kinds = [k for k, bit in ((TGT, 1), (SRC, 2), (REF, 4)) if qr & bit]
@@ -210,3 +226,21 @@ def test_stream_layout_sequence():
         keys.append(st["useful_pairs"] / w.H / (w.C * w.T))
     assert keys[:5] == [7800, 12480, 17160, 21840, 26520]
     assert all(k == 26520 for k in keys[4:])
+
+
+def test_stream_layout_sequence_with_sink():
+    """A stream keeping 2 sink frames beside a 4-frame window (ring of 7 frames): per-row
+    history grows to sink + window frames and stays there, and the driver's ring bookkeeping
+    (what fa_stream_state reports) matches the ring layout."""
+    T, C, win, cap, S = 16, 2, 4, 7, 2
+    d = B.make_desc(C, T, 1, 64, chunk_start=0, window=win, cache_frames=cap, query_rows=1,
+                    dtype=B.FA_F32, sink_frames=S)
+    s = B.Stream(d)
+    for cs in range(0, 20, C):
+        nf, rf = s.state()
+        assert nf == cs
+        assert rf == max(0, cs - (cap - S))
+        st = B.fa_layout_stats(s.layout())
+        hist = len(set(range(max(0, cs - win), cs)) | set(range(min(S, cs))))
+        assert st["useful_pairs"] == (hist + C) * T * C * T + C * T * T
+        s.seek(cs + C, max(rf, cs + C - (cap - S)))
