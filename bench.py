@@ -246,6 +246,69 @@ def time_lowbit_chunk(torch, W, B, reps=10):
             "chunk_useful_tops": round(ops / (q_ms + a_ms) / 1e9, 2)}
 
 
+def time_graph_chunk(torch, W, B, lowbit, reps=20):
+    """The steady chunk's per-chunk sequence -- (quantise ->) attention -> ring append -- launched
+    eagerly and as one captured HIP graph replayed; ms per chunk for both."""
+    w = W.WORKLOADS[4 if lowbit else 2]
+    cs = (w.chunks - 1) * w.C
+    dev = lambda x: torch.from_numpy(x).unsqueeze(0).to("cuda").to(torch.bfloat16).contiguous()
+    x = W.chunk_tensors(w, cs // w.C)
+    r = W.ref_tensors(w)
+    t = {n: dev(v) for n, v in {**x, **r}.items()}
+    for n in ("k_ring", "v_ring"):
+        t[n] = torch.randn((1, w.cache_frames * w.T, w.H, w.D), device="cuda").to(torch.bfloat16)
+    d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=cs,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=1,
+                    dtype=B.FA_LOWBIT if lowbit else B.FA_BF16)
+    L = B.fa_layout_build(d)
+    B.fa_layout_prepare(L)
+    rows = w.C * w.T
+    out = {"o_tgt": torch.empty((1, rows, w.H, w.D), dtype=torch.bfloat16, device="cuda"),
+           "lse_tgt": torch.empty((1, w.H, rows), dtype=torch.float32, device="cuda")}
+    if lowbit:
+        codes, scales = {}, {}
+        for n, v in t.items():
+            codes[n] = torch.empty(v.shape, dtype=torch.uint8 if n.startswith("v_") else torch.int8,
+                                   device="cuda")
+            scales[n] = torch.empty((1, w.H, (v.shape[1] + 127) // 128), dtype=torch.float32,
+                                    device="cuda")
+        extra = {"k_mean": torch.empty((1, w.H, w.D), dtype=torch.float32, device="cuda"),
+                 "v_absmax": torch.empty((1, w.H), dtype=torch.float32, device="cuda")}
+        io_in = B.make_io(t)
+        io_q = B.make_io({**codes, "lse_tgt": out["lse_tgt"], **extra}, scales)
+        io_a = B.make_io({**codes, **out, "v_absmax": extra["v_absmax"]}, scales)
+    else:
+        io_a = B.make_io({**t, **out})
+
+    def seq():
+        if lowbit:
+            B.fa_quantize_lowbit(L, io_in, io_q, 0)
+        B.fa_attn_fwd(L, io_a)
+        B.fa_ring_append(d, t["k_ring"], t["v_ring"], t["k_tgt"], t["v_tgt"], cs, w.C)
+
+    def timed(fn):
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return statistics.median([e[0].elapsed_time(e[1]) for e in ev])
+
+    eager = timed(seq)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    graph = timed(g.replay)
+    return {"workload": w.name + " per-chunk sequence (steady chunk, cs=%d)" % cs,
+            "kernels": 5 if lowbit else 2, "eager_ms": round(eager, 4),
+            "graph_replay_ms": round(graph, 4), "saved_us": round((eager - graph) * 1e3, 1)}
+
+
 def cpu_baseline(W, budget_s):
     """The oracle, as it stands, on a bounded sample of the steady chunk (chunk 19)."""
     import numpy as np
@@ -439,7 +502,9 @@ def main():
         log("bench: other bf16 workloads")
         out["other_workloads"] = [time_single_call(1, torch, W, B), time_single_call(3, torch, W, B),
                                   time_lowbit_chunk(torch, W, B),
-                                  time_single_call(2, torch, W, B, sink=3)]
+                                  time_single_call(2, torch, W, B, sink=3),
+                                  time_graph_chunk(torch, W, B, False),
+                                  time_graph_chunk(torch, W, B, True)]
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)

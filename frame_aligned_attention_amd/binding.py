@@ -87,6 +87,7 @@ def _load():
         "fa_layout_tile": ([P, C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
                             C.c_int32], C.c_int),
         "fa_layout_destroy": ([P], C.c_int),
+        "fa_layout_prepare": ([P], C.c_int),
         "fa_attn_fwd": ([P, C.POINTER(fa_io), P], C.c_int),
         "fa_quantize_lowbit": ([P, C.POINTER(fa_io), C.POINTER(fa_io), C.c_int32, P], C.c_int),
         "fa_ring_append": ([C.POINTER(fa_layout_desc)] + [C.POINTER(fa_tensor)] * 4 +
@@ -218,6 +219,10 @@ def fa_layout_destroy(L: Layout):
     if L.handle:
         _check(lib.fa_layout_destroy(L.handle), "fa_layout_destroy")
         L.handle = None
+
+
+def fa_layout_prepare(L: Layout):
+    _check(lib.fa_layout_prepare(L.handle), "fa_layout_prepare")
 
 
 def fa_attn_fwd(L: Layout, io: fa_io, stream=None):

@@ -106,8 +106,14 @@ static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t strea
   a.scale = d.scale;
   a.c = d.scale * 1.4426950408889634f;
   if (L->work.empty()) return FA_OK;
+  // Under stream capture the block map must already be on the device (fa_layout_prepare).
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    capture = hipStreamCaptureStatusNone;
+  }
   DeviceMap m;
-  fa_status st = device_map(L, &m);
+  fa_status st = device_map(L, &m, capture == hipStreamCaptureStatusNone);
   if (st != FA_OK) return st;
   a.tiles = m.tiles;
   a.ranges = m.ranges;

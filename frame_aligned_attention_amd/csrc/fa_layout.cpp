@@ -244,7 +244,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   return FA_OK;
 }
 
-fa_status device_map(const fa_layout *L, DeviceMap *out) {
+fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> g(L->mu);
@@ -253,6 +253,10 @@ fa_status device_map(const fa_layout *L, DeviceMap *out) {
     *out = it->second;
     return FA_OK;
   }
+  if (!may_upload)
+    return fail(FA_ERR_INVALID,
+                "the layout's block map is not on this device yet: call fa_layout_prepare "
+                "before capturing the stream");
   DeviceMap m;
   const size_t nt = std::max<size_t>(1, L->tiles.size()), nr = std::max<size_t>(1, L->ranges.size()),
                nw = std::max<size_t>(1, L->work.size());
@@ -288,6 +292,13 @@ fa_status device_map(const fa_layout *L, DeviceMap *out) {
 }  // namespace fa
 
 using namespace fa;
+
+extern "C" fa_status fa_layout_prepare(const fa_layout *L) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (L->work.empty()) return FA_OK;
+  DeviceMap m;
+  return device_map(L, &m, true);
+}
 
 extern "C" fa_status fa_layout_build(const fa_layout_desc *d, int32_t ring_first_frame,
                                      fa_layout **out) {

@@ -39,5 +39,7 @@ struct fa_layout {
 
 namespace fa {
 // Device copy of L's block map for the current device (uploaded on first use).
-fa_status device_map(const fa_layout *L, DeviceMap *out);
+// The layout's block map on the current device.  Uploads it on first use unless may_upload is
+// false (a stream being captured into a graph must not allocate or copy synchronously).
+fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload = true);
 }  // namespace fa

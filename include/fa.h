@@ -148,6 +148,19 @@ const char *fa_last_error(void);
 fa_status fa_layout_build(const fa_layout_desc *d, int32_t ring_first_frame, fa_layout **out);
 
 /*
+ * Puts the layout's block map on the current device now (a synchronous
+ * allocation and copy, done once per device), so that later fa_attn_fwd
+ * calls with it allocate and copy nothing.  Needed before a stream that
+ * launches fa_attn_fwd is captured into a HIP graph (the launch optimisation
+ * of the tech report's fusion-and-graphs paragraph and the launch article's
+ * technical-stack section): under capture, fa_attn_fwd with a map not yet on
+ * the device returns FA_ERR_INVALID instead of allocating.  fa_ring_append
+ * and fa_quantize_lowbit need no preparation.  FA_ERR_NOMEM / FA_ERR_HIP on
+ * device failures.
+ */
+fa_status fa_layout_prepare(const fa_layout *L);
+
+/*
  * Work counts of a layout: useful (query, key) pairs and useful FLOPs
  * (4*head_dim per pair, all heads and batches), keys the kernel visits
  * (pairs including masked entries of partial tiles), and the algorithmic
@@ -189,7 +202,9 @@ fa_status fa_layout_destroy(fa_layout *L);
  * tensors directly; FA_LOWBIT reads the codes and scales written by
  * fa_quantize_lowbit (q/k int8, v e4m3) and writes bf16 O.  Rows with no
  * visible key (impossible under the rule unless T = 0) get O = 0, LSE = -inf.
- * Allocates nothing; asynchronous.
+ * The first call with a layout on a device uploads its block map (unless
+ * fa_layout_prepare did); after that it allocates and copies nothing.
+ * Asynchronous.
  */
 fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
 
