@@ -238,8 +238,17 @@ def time_lowbit_chunk(torch, W, B, reps=10):
     torch.cuda.synchronize()
     q_ms = statistics.median([e[0].elapsed_time(e[1]) for e in ev])
     a_ms = statistics.median([e[1].elapsed_time(e[2]) for e in ev])
+    # the same quantiser with the key mean supplied (a mean fixed per stream, FA_QUANT_MEAN_GIVEN)
+    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in evg:
+        e[0].record(stream)
+        B.fa_quantize_lowbit(L, io_in, io_q, B.FA_QUANT_MEAN_GIVEN, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    qg_ms = statistics.median([e[0].elapsed_time(e[1]) for e in evg])
     ops = B.fa_layout_stats(L)["useful_flops"]
     return {"workload": w.name + " (steady chunk, cs=57)", "quantise_ms": round(q_ms, 4),
+            "quantise_ms_mean_given": round(qg_ms, 4),
             "attn_ms": round(a_ms, 4), "chunk_ms": round(q_ms + a_ms, 4),
             "attn_useful_tops": round(ops / a_ms / 1e9, 2),
             "attn_frac_of_5000_tops": round(ops / a_ms / 1e9 / PEAK_I8_F8_TOPS, 4),

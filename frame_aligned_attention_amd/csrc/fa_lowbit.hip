@@ -35,13 +35,21 @@ __global__ void __launch_bounds__(64) quant_init_kernel(float *v_absmax, int n) 
   if (i < n) v_absmax[i] = 0.0f;
 }
 
-// Per-(batch, head) channel mean of the keys in view.  One workgroup per (b, h, 8 channels):
-// 256 token lanes each sum a strided share in fp32, then a fixed-order tree: deterministic.
-__global__ void __launch_bounds__(256) kmean_kernel(const QuantArgs a) {
-  const int nchunk = a.D / 8;
-  const int bh = blockIdx.x / nchunk, ch = (blockIdx.x % nchunk) * 8;
+// Per-(batch, head) channel mean of the keys in view.  kMeanSplit workgroups of 1024 threads
+// per (b, h), each over 128/kMeanSplit channels: LPR lanes read a token row's slice (16 bytes
+// each), SLOTS row slots walk the tokens with four loads in flight per lane, each lane sums its
+// 8 channels in fp32 in a fixed order, then a fixed-order tree over the row slots:
+// deterministic.
+constexpr int kMeanThreads = 1024;
+constexpr int kMeanSplit = 4;
+__global__ void __launch_bounds__(kMeanThreads) kmean_kernel(const QuantArgs a) {
+  constexpr int CPW = 128 / kMeanSplit;  // channels per workgroup
+  constexpr int LPR = CPW / 8;           // lanes per token row
+  constexpr int SLOTS = kMeanThreads / LPR;
+  const int bh = blockIdx.x / kMeanSplit, c0 = (blockIdx.x % kMeanSplit) * CPW;
   const int b = bh / a.H, h = bh % a.H;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lanec = t % LPR, slot = t / LPR;
+  const int ch = c0 + lanec * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int count = 0;
   for (int si = 0; si < a.nseg; ++si) {
@@ -49,84 +57,107 @@ __global__ void __launch_bounds__(256) kmean_kernel(const QuantArgs a) {
     if (g.kind != 1) continue;
     for (int run = 0; run < 2; ++run) {
       const int lo = run ? g.lo1 : g.lo0, hi = run ? g.hi1 : g.hi0;
-      if (hi > lo) count += hi - lo;
-      for (int tok = lo + t; tok < hi; tok += 256) {
-        const __bf16 *p =
-            (const __bf16 *)g.in + b * g.isb + (int64_t)tok * g.isn + h * g.ish + ch;
-        const bf16x8_t v = *(const bf16x8_t *)p;
+      if (hi <= lo) continue;
+      count += hi - lo;
+      const __bf16 *base = (const __bf16 *)g.in + b * g.isb + h * g.ish + ch;
+      int tok = lo + slot;
+      for (; tok + 3 * SLOTS < hi; tok += 4 * SLOTS) {
+        bf16x8_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = *(const bf16x8_t *)(base + (int64_t)(tok + u * SLOTS) * g.isn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += (float)v[u][i];
+      }
+      for (; tok < hi; tok += SLOTS) {
+        const bf16x8_t v = *(const bf16x8_t *)(base + (int64_t)tok * g.isn);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
       }
     }
   }
-  __shared__ float red[256][9];
+  // red[slot][channel of the slice]; slots summed pairwise in a fixed order
+  __shared__ float red[SLOTS][CPW + 1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[t][i] = acc[i];
+  for (int i = 0; i < 8; ++i) red[slot][lanec * 8 + i] = acc[i];
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) red[t][i] += red[t + w][i];
+  for (int w = SLOTS / 2; w > 0; w >>= 1) {
+    for (int e = t; e < w * CPW; e += kMeanThreads) {
+      const int s_ = e / CPW, c = e % CPW;
+      red[s_][c] += red[s_ + w][c];
     }
     __syncthreads();
   }
-  if (t < 8) a.k_mean[(int64_t)bh * a.D + ch + t] = count ? red[0][t] / (float)count : 0.0f;
+  if (t < CPW) a.k_mean[(int64_t)bh * a.D + c0 + t] = count ? red[0][t] / (float)count : 0.0f;
 }
 
 __device__ __forceinline__ bool in_runs(const QSeg &g, int tok) {
   return (tok >= g.lo0 && tok < g.hi0) || (tok >= g.lo1 && tok < g.hi1);
 }
 
-// One workgroup per (tensor, 128-token block, batch, head): 2 threads per token, 64 channels each.
+// One workgroup per (tensor, 128-token block, batch, head).  16 lanes cover the 256 bytes of a
+// token row (8 channels each), so a wave reads 4 whole rows per load; 16 rows per pass, 8
+// passes per block.
 __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
-  const int per_bh = a.total_blocks;
-  const int bh = blockIdx.x / per_bh, flat = blockIdx.x % per_bh;
+  // heads vary fastest along the grid: workgroups running together read neighbouring pieces of
+  // the same token rows
+  const int nbh = a.batch * a.H;
+  const int bh = blockIdx.x % nbh, flat = blockIdx.x / nbh;
   const int b = bh / a.H, h = bh % a.H;
   int si = 0;
   while (si + 1 < a.nseg && a.seg[si + 1].blk_begin <= flat) ++si;
   const QSeg &g = a.seg[si];
   const int blk = flat - g.blk_begin;
-  const int t = threadIdx.x;
-  const int tok = blk * 128 + (t >> 1), c0 = (t & 1) * 64;
-  const bool live = in_runs(g, tok);
-  float x[64];
+  const int t = threadIdx.x, lane16 = t & 15, rsub = t >> 4;
+  const int c0 = lane16 * 8;
+  const bool need_m = g.kind == 1 || (g.kind == 0 && g.lse);
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = need_m ? a.k_mean[(int64_t)bh * a.D + c0 + i] : 0.0f;
+  float x[8][8];
+  bool live[8];
   float amax = 0.0f;
-  if (live) {
-    const __bf16 *p = (const __bf16 *)g.in + b * g.isb + (int64_t)tok * g.isn + h * g.ish + c0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8_t v = *(const bf16x8_t *)(p + 8 * j);
+  for (int j = 0; j < 8; ++j) {
+    const int tok = blk * 128 + j * 16 + rsub;
+    live[j] = in_runs(g, tok);
+    if (live[j]) {
+      const bf16x8_t v = *(const bf16x8_t *)((const __bf16 *)g.in + b * g.isb +
+                                             (int64_t)tok * g.isn + h * g.ish + c0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[8 * j + i] = (float)v[i];
+      for (int i = 0; i < 8; ++i) x[j][i] = g.kind == 1 ? (float)v[i] - m[i] : (float)v[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[j][i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[j][i] = 0.0f;
     }
-    if (g.kind == 1) {
-      const float *m = a.k_mean + (int64_t)bh * a.D + c0;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = x[i] - m[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
   }
   if (g.kind == 0 && g.lse) {
     // the LSE the kernel computes is that of the smoothed scores q.(k - m); record the
     // per-row shift scale * q.m, which the attention kernel adds back
-    const float *m = a.k_mean + (int64_t)bh * a.D + c0;
-    float dot = 0.0f;
-    if (live) {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) dot = fmaf(x[i], m[i], dot);
+    for (int j = 0; j < 8; ++j) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot = fmaf(x[j][i], m[i], dot);
+      dot += __shfl_xor(dot, 8);
+      dot += __shfl_xor(dot, 4);
+      dot += __shfl_xor(dot, 2);
+      dot += __shfl_xor(dot, 1);
+      if (live[j] && lane16 == 0)
+        g.lse[(int64_t)bh * g.n + blk * 128 + j * 16 + rsub] = a.softmax_scale * dot;
     }
-    dot += __shfl_xor(dot, 1);
-    if (live && (t & 1) == 0) g.lse[(int64_t)bh * g.n + tok] = a.softmax_scale * dot;
   }
-  __shared__ float red[256];
-  red[t] = amax;
+  // block absmax: across the wave, then across the four waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  __shared__ float red[4];
+  if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-    __syncthreads();
-  }
-  amax = red[0];
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float qmax = g.kind == 2 ? 448.0f : 127.0f;
   const float scale = amax / qmax;
   const float inv = amax > 0.0f ? qmax / amax : 0.0f;
@@ -134,37 +165,40 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
     g.scale[(int64_t)bh * g.nblk + blk] = scale;
     if (g.kind == 2) atomicMax((unsigned int *)(a.v_absmax + bh), __float_as_uint(scale));
   }
-  if (!live) return;
-  uint32_t w32[16];
-  if (g.kind == 2) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i] * inv, x[4 * i + 1] * inv, 0, false);
-      v = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2] * inv, x[4 * i + 3] * inv, v, true);
-      w32[i] = (uint32_t)v;
-    }
-  } else {
+  for (int j = 0; j < 8; ++j) {
+    if (!live[j]) continue;
+    uint32_t w32[2];
+    if (g.kind == 2) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float r = fminf(fmaxf(__builtin_rintf(x[4 * i + j] * inv), -127.0f), 127.0f);
-        v |= ((uint32_t)(int)r & 0xffu) << (8 * j);
+      for (int k = 0; k < 2; ++k) {
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[j][4 * k] * inv, x[j][4 * k + 1] * inv, 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(x[j][4 * k + 2] * inv, x[j][4 * k + 3] * inv, v, true);
+        w32[k] = (uint32_t)v;
       }
-      w32[i] = v;
-    }
-  }
-  char *o = (char *)g.out + b * g.osb + (int64_t)tok * g.osn + h * g.osh + c0;
+    } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *(uint4 *)(o + 16 * j) = uint4{w32[4 * j], w32[4 * j + 1], w32[4 * j + 2], w32[4 * j + 3]};
+      for (int k = 0; k < 2; ++k) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float r = fminf(fmaxf(__builtin_rintf(x[j][4 * k + i] * inv), -127.0f), 127.0f);
+          v |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+        }
+        w32[k] = v;
+      }
+    }
+    const int tok = blk * 128 + j * 16 + rsub;
+    char *o = (char *)g.out + b * g.osb + (int64_t)tok * g.osn + h * g.osh + c0;
+    *(uint2 *)o = uint2{w32[0], w32[1]};
+  }
 }
 
 hipError_t launch_quant_lowbit(const QuantArgs &a, bool mean_given, hipStream_t s) {
   const int nbh = a.batch * a.H;
   hipLaunchKernelGGL(quant_init_kernel, dim3((nbh + 63) / 64), dim3(64), 0, s, a.v_absmax, nbh);
-  if (!mean_given) hipLaunchKernelGGL(kmean_kernel, dim3(nbh * (a.D / 8)), dim3(256), 0, s, a);
+  if (!mean_given)
+    hipLaunchKernelGGL(kmean_kernel, dim3(nbh * kMeanSplit), dim3(kMeanThreads), 0, s, a);
   if (a.total_blocks > 0)
     hipLaunchKernelGGL(quant_kernel, dim3(nbh * a.total_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
