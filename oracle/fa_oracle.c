@@ -281,6 +281,50 @@ void fa_oracle_quant_e4m3(const float *x, int N, int H, int D, const float *mean
   quant_blocks(x, N, H, D, mean, 448.0f, 1, codes, scales);
 }
 
+void fa_oracle_quant_int8_2d(const float *x, int rows, int cols, int br, int bc, int8_t *codes,
+                             float *scales) {
+  const int nbr = (rows + br - 1) / br, nbc = (cols + bc - 1) / bc;
+  int bi, bj, i, j;
+  for (bi = 0; bi < nbr; ++bi)
+    for (bj = 0; bj < nbc; ++bj) {
+      const int i0 = bi * br, i1 = i0 + br < rows ? i0 + br : rows;
+      const int j0 = bj * bc, j1 = j0 + bc < cols ? j0 + bc : cols;
+      float absmax = 0.0f, inv;
+      for (i = i0; i < i1; ++i)
+        for (j = j0; j < j1; ++j) {
+          const float a = fabsf(x[(long)i * cols + j]);
+          if (a > absmax) absmax = a;
+        }
+      scales[(long)bi * nbc + bj] = absmax / 127.0f;
+      inv = absmax > 0.0f ? 127.0f / absmax : 0.0f;
+      for (i = i0; i < i1; ++i)
+        for (j = j0; j < j1; ++j) {
+          float r = nearbyintf(x[(long)i * cols + j] * inv); /* ties to even */
+          if (r > 127.0f) r = 127.0f;
+          if (r < -127.0f) r = -127.0f;
+          codes[(long)i * cols + j] = (int8_t)r;
+        }
+    }
+}
+
+void fa_oracle_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
+                         int m, int n, int k, double *y) {
+  const int kb = (k + 127) / 128;
+  int i, j, b, t;
+#pragma omp parallel for private(j, b, t) schedule(static)
+  for (i = 0; i < m; ++i)
+    for (j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (b = 0; b < kb; ++b) {
+        long dot = 0;
+        const int t1 = (b + 1) * 128 < k ? (b + 1) * 128 : k;
+        for (t = b * 128; t < t1; ++t) dot += (long)xq[(long)i * k + t] * wq[(long)j * k + t];
+        acc += (double)sx[(long)i * kb + b] * (double)sw[(long)(j / 128) * kb + b] * (double)dot;
+      }
+      y[(long)i * n + j] = acc;
+    }
+}
+
 /* OCP e4m3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits.  Normal
  * values 2^(e-7) * (1 + m/8) for e = 1..15 (except e=15,m=7 which is NaN),
  * subnormals 2^-6 * m/8.  Largest finite 448.  Encoding here: round to the

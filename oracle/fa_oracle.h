@@ -110,6 +110,28 @@ void fa_oracle_quant_int8(const float *x, int N, int H, int D, const float *mean
                           int8_t *codes, float *scales);
 void fa_oracle_quant_e4m3(const float *x, int N, int H, int D, const float *mean,
                           uint8_t *codes, float *scales);
+/*
+ * Per-block W8A8 linear layer (tech report, paragraph on linear layers: a
+ * per-block W8A8 GEMM whose fine-grained scales keep outliers from setting
+ * the range of a whole tensor or channel).  Reading: int8 codes with one fp32
+ * scale per block, activations in blocks of 1 row x 128 columns, weights in
+ * blocks of 128 x 128, both quantised like the attention path (scale
+ * absmax/127, code = round_half_even(x * (127/absmax)) clamped to +-127).
+ *
+ * fa_oracle_quant_int8_2d: row-major [rows][cols] in blocks of br x bc (edge
+ * blocks partial); scales [ceil(rows/br)][ceil(cols/bc)] row-major.
+ */
+void fa_oracle_quant_int8_2d(const float *x, int rows, int cols, int br, int bc, int8_t *codes,
+                             float *scales);
+/*
+ * y[i][j] = sum over 128-column blocks b of sx[i][b] * sw[j/128][b] *
+ * (sum over k in block b of xq[i][k] * wq[j][k]), the inner sums exact in
+ * integers, the rest in double.  xq [m][k], wq [n][k], sx [m][kb],
+ * sw [ceil(n/128)][kb] with kb = ceil(k/128); y [m][n].
+ */
+void fa_oracle_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
+                         int m, int n, int k, double *y);
+
 /* OCP e4m3 (bias 7, no infinities, 0x7f/0xff NaN, max 448): RNE, saturating. */
 uint8_t fa_oracle_e4m3_encode(float x);
 float fa_oracle_e4m3_decode(uint8_t c);

@@ -62,6 +62,11 @@ def _bind(path: str):
     lib.fa_oracle_e4m3_decode.argtypes = [C.c_uint8]
     lib.fa_oracle_e4m3_decode.restype = C.c_float
     lib.fa_oracle_kmean.argtypes = [C.c_int, C.POINTER(fp), ip, C.c_int, C.c_int, fp]
+    lib.fa_oracle_quant_int8_2d.argtypes = [fp, C.c_int, C.c_int, C.c_int, C.c_int,
+                                            C.POINTER(C.c_int8), fp]
+    i8p = C.POINTER(C.c_int8)
+    lib.fa_oracle_w8a8_gemm.argtypes = [i8p, fp, i8p, fp, C.c_int, C.c_int, C.c_int,
+                                        C.POINTER(C.c_double)]
     return lib
 
 
@@ -245,3 +250,32 @@ def kmean(segs, lib=None):
     mean = np.zeros((H, D), np.float32)
     lib.fa_oracle_kmean(len(segs), arr, ntok, H, D, _fp(mean))
     return mean
+
+
+def quant_int8_2d(x, br, bc, lib=None):
+    """Per-block int8 of a [rows, cols] matrix in br x bc blocks -> (codes int8 [rows, cols],
+    scales [ceil(rows/br), ceil(cols/bc)])."""
+    lib = lib or load()
+    x = _f32(x)
+    rows, cols = x.shape
+    codes = np.zeros(x.shape, np.int8)
+    scales = np.zeros(((rows + br - 1) // br, (cols + bc - 1) // bc), np.float32)
+    lib.fa_oracle_quant_int8_2d(_fp(x), rows, cols, br, bc,
+                                codes.ctypes.data_as(C.POINTER(C.c_int8)), _fp(scales))
+    return codes, scales
+
+
+def w8a8_gemm(xq, sx, wq, sw, lib=None):
+    """Per-block W8A8 product: xq [m,k] int8, sx [m, ceil(k/128)], wq [n,k] int8,
+    sw [ceil(n/128), ceil(k/128)] -> y [m,n] float64."""
+    lib = lib or load()
+    xq = np.ascontiguousarray(xq, np.int8)
+    wq = np.ascontiguousarray(wq, np.int8)
+    sx, sw = _f32(sx), _f32(sw)
+    m, k = xq.shape
+    n = wq.shape[0]
+    y = np.zeros((m, n), np.float64)
+    i8p = C.POINTER(C.c_int8)
+    lib.fa_oracle_w8a8_gemm(xq.ctypes.data_as(i8p), _fp(sx), wq.ctypes.data_as(i8p), _fp(sw),
+                            m, n, k, y.ctypes.data_as(C.POINTER(C.c_double)))
+    return y

@@ -21,6 +21,8 @@ What pins what:
                     exactly the sink and window frames matter
   smoothing         subtracting a per-channel vector from all keys is exact
   quantiser         hand-derived codes, round-trip bound, torch float8_e4m3fn
+  W8A8              hand-derived block codes, torch round; integer matmul (numpy), per-block
+                    scale weighting, closed-form quantisation error bound
 """
 from __future__ import annotations
 
@@ -530,7 +532,70 @@ def pin_kmean(lib):
     close(m, want, 1e-7, "kmean")
 
 
+def pin_w8a8_quant(lib):
+    """Per-block int8 of matrices: hand-derived codes (scale absmax/127, ties to even, clamp),
+    block shapes 1 x 128 and 128 x 128 with partial edges, and torch's half-to-even round."""
+    x = np.zeros((2, 130), np.float32)
+    x[0, :8] = [127, -63.5, 0.5, 1.5, 2.5, -2.5, 100, 0]       # absmax 127: inv 1
+    x[0, 128:] = [3, -1]                                        # second block: absmax 3
+    x[1, :4] = [254, 3, 5, 7]                                   # absmax 254: inv 1/2
+    codes, scales = O.quant_int8_2d(x, 1, 128, lib=lib)
+    assert codes[0, :8].tolist() == [127, -64, 0, 2, 2, -2, 100, 0], codes[0, :8]
+    assert codes[0, 128:].tolist() == [127, -42], codes[0, 128:]  # -1 * 127/3 = -42.33
+    assert codes[1, :4].tolist() == [127, 2, 2, 4], codes[1, :4]  # 1.5, 2.5, 3.5 -> 2, 2, 4
+    assert scales.shape == (2, 2)
+    assert scales[0, 0] == np.float32(127) / np.float32(127) and scales[1, 0] == np.float32(2)
+    assert scales[0, 1] == np.float32(3) / np.float32(127) and scales[1, 1] == 0.0
+    g = np.random.default_rng(5)
+    w = (g.standard_normal((200, 260)) * np.exp(g.standard_normal((200, 1)))).astype(np.float32)
+    for br, bc in ((1, 128), (128, 128), (64, 32)):
+        codes, scales = O.quant_int8_2d(w, br, bc, lib=lib)
+        for bi in range(scales.shape[0]):
+            for bj in range(scales.shape[1]):
+                blk = torch.from_numpy(w[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc])
+                amax = blk.abs().max()
+                assert scales[bi, bj] == (amax / 127).item()
+                want = torch.clamp(torch.round(blk * (127 / amax)), -127, 127).to(torch.int8)
+                got = codes[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc]
+                assert np.array_equal(got, want.numpy()), (br, bc, bi, bj)
+
+
+def pin_w8a8_gemm(lib):
+    """The W8A8 product: with unit scales it is the integer matmul (numpy int64); with scales,
+    the scale-weighted sum of per-block integer matmuls; the dequantised product stays within
+    the closed-form quantisation error bound of the float product."""
+    g = np.random.default_rng(6)
+    m, n, k = 7, 256, 384
+    xq = g.integers(-127, 128, size=(m, k)).astype(np.int8)
+    wq = g.integers(-127, 128, size=(n, k)).astype(np.int8)
+    y = O.w8a8_gemm(xq, np.ones((m, 3), np.float32), wq, np.ones((2, 3), np.float32), lib=lib)
+    assert np.array_equal(y, (xq.astype(np.int64) @ wq.astype(np.int64).T).astype(np.float64))
+    sx = g.uniform(0.01, 2, size=(m, 3)).astype(np.float32)
+    sw = g.uniform(0.01, 2, size=(2, 3)).astype(np.float32)
+    y = O.w8a8_gemm(xq, sx, wq, sw, lib=lib)
+    want = np.zeros((m, n))
+    for b in range(3):
+        part = xq[:, b * 128:(b + 1) * 128].astype(np.int64) @ wq[:, b * 128:(b + 1) * 128].astype(
+            np.int64).T
+        want += sx[:, b:b + 1].astype(np.float64) * np.repeat(sw[:, b].astype(np.float64), 128)[
+            None, :] * part
+    close(y, want, 1e-12, "W8A8 = scale-weighted per-block integer products")
+    # quantise float matrices and compare with the float product: |x.w - xq.wq| is bounded by
+    # sum_k |x||dw| + |dx||w| + |dx||dw| with |dx| <= sx/2, |dw| <= sw/2 per block
+    x = g.standard_normal((m, k)).astype(np.float32)
+    w = g.standard_normal((n, k)).astype(np.float32)
+    xq, sx = O.quant_int8_2d(x, 1, 128, lib=lib)
+    wq, sw = O.quant_int8_2d(w, 128, 128, lib=lib)
+    y = O.w8a8_gemm(xq, sx, wq, sw, lib=lib)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    dx = np.repeat(sx.astype(np.float64), 128, 1)[:, :k] / 2 * (1 + 1e-6)
+    dw = np.repeat(np.repeat(sw.astype(np.float64), 128, 0)[:n], 128, 1)[:, :k] / 2 * (1 + 1e-6)
+    bound = np.abs(x) @ dw.T + dx @ np.abs(w).T + dx @ dw.T
+    assert np.all(np.abs(y - exact) <= bound + 1e-9)
+    assert np.abs(y - exact).max() > 0  # the quantisation did something
+
+
 ALL_PINS = [pin_golden_masks, pin_bruteforce, pin_f1_full_attention, pin_two_keys,
             pin_large_scores, pin_q_zero,
             pin_ones_v, pin_perturbations, pin_permutation, pin_split_merge,
-            pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean]
+            pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean, pin_w8a8_quant, pin_w8a8_gemm]

@@ -48,6 +48,11 @@ MUTANTS = {
                      "(kframe >= history_lo(p))"),
     "sink off by one": ("(kframe >= history_lo(p) || kframe < p->sink)",
                         "(kframe >= history_lo(p) || kframe <= p->sink)"),
+    "w8a8 weight scale by row block": (
+        "(double)sw[(long)(j / 128) * kb + b]", "(double)sw[(long)(i / 128) * kb + b]"),
+    "w8a8 activation scale dropped": ("acc += (double)sx[(long)i * kb + b] * ", "acc += "),
+    "w8a8 block of 64": ("int t1 = (b + 1) * 128 < k ? (b + 1) * 128 : k;",
+                         "int t1 = (b + 1) * 128 - 64 < k ? (b + 1) * 128 - 64 : k;"),
     "kmean off by one": ("mean[h * D + d] = n ? (float)(acc / (double)n) : 0.0f;",
                          "mean[h * D + d] = n ? (float)(acc / (double)(n + 1)) : 0.0f;"),
 }
