@@ -318,6 +318,47 @@ def time_graph_chunk(torch, W, B, lowbit, reps=20):
             "graph_replay_ms": round(graph, 4), "saved_us": round((eager - graph) * 1e3, 1)}
 
 
+def time_w8a8(torch, W, B, reps=10):
+    """Per-block W8A8 QKV projection of a stream chunk: activation quantiser and int8 GEMM;
+    useful ops 2*m*n*k against the dense int8 MFMA peak.  torch's bf16 matmul of the same
+    shape is timed beside it for context."""
+    wl = W.W8A8_QKV
+    m, n, k = wl.m, wl.n, wl.k
+    x, w = W.linear_tensors(1, m, n, k)
+    xd = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+    wd = torch.from_numpy(w).to("cuda").to(torch.bfloat16)
+    xq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    wq = torch.empty((n, k), dtype=torch.int8, device="cuda")
+    sx = torch.empty((k // 128, m), dtype=torch.float32, device="cuda")
+    sw = torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    B.fa_w8a8_quantize_weight(wd, wq, sw)
+    wt = wd.t().contiguous()  # w^T [k, n] as a plain contiguous operand
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return statistics.median([e[0].elapsed_time(e[1]) for e in ev])
+
+    q_ms = timed(lambda: B.fa_w8a8_quantize_act(xd, xq, sx))
+    g_ms = timed(lambda: B.fa_w8a8_gemm(xq, sx, wq, sw, y))
+    bf_ms = timed(lambda: torch.mm(xd, wt))
+    ops = 2.0 * m * n * k
+    return {"workload": wl.name + " (QKV projection of a 1560-token 40-head chunk)",
+            "quantise_act_ms": round(q_ms, 4), "gemm_ms": round(g_ms, 4),
+            "gemm_tops": round(ops / g_ms / 1e9, 1),
+            "gemm_frac_of_5000_tops": round(ops / g_ms / 1e9 / PEAK_I8_F8_TOPS, 4),
+            "quantise_plus_gemm_ms": round(q_ms + g_ms, 4),
+            "torch_bf16_mm_ms": round(bf_ms, 4)}
+
+
 def cpu_baseline(W, budget_s):
     """The oracle, as it stands, on a bounded sample of the steady chunk (chunk 19)."""
     import numpy as np
@@ -513,7 +554,8 @@ def main():
                                   time_lowbit_chunk(torch, W, B),
                                   time_single_call(2, torch, W, B, sink=3),
                                   time_graph_chunk(torch, W, B, False),
-                                  time_graph_chunk(torch, W, B, True)]
+                                  time_graph_chunk(torch, W, B, True),
+                                  time_w8a8(torch, W, B)]
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)

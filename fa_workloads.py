@@ -144,3 +144,32 @@ def ref_tensors(w: Workload, H: int | None = None, ref_tokens: List[int] | None 
 
 def stream_chunk_starts(w: Workload) -> List[int]:
     return [w.first_cs + i * w.C for i in range(w.chunks)]
+
+
+# ---------------------------------------------------------------- per-block W8A8 linear layer
+
+@dataclass
+class LinearWorkload:
+    """A linear layer y = x . w^T: x [m, k] activations, w [n, k] weights."""
+    name: str
+    m: int
+    n: int
+    k: int
+
+
+# The QKV projection of one chunk of the 1560-token 40-head stream: target and source tokens of
+# a 3-frame chunk (2 x 4680 rows), hidden size 40 x 128, output Q, K and V (3 x 5120).
+W8A8_QKV = LinearWorkload("w8a8-qkv-9360x5120x15360", m=9360, n=15360, k=5120)
+
+
+def linear_tensors(seed: int, m: int, n: int, k: int):
+    """Seeded bf16-rounded activations and weights.  Activations: N(0,1) times a per-row
+    log-normal scale, plus sparse large outliers (1 in 500 entries times 20), the case
+    per-block scales are for; weights: N(0, 1/k)."""
+    g = np.random.default_rng([1000, int(seed)])
+    x = g.standard_normal((m, k), dtype=np.float32)
+    x *= np.exp(0.5 * g.standard_normal((m, 1))).astype(np.float32)
+    out = g.random((m, k)) < 0.002
+    x[out] *= 20.0
+    w = (g.standard_normal((n, k), dtype=np.float32) / np.float32(np.sqrt(k)))
+    return round_bf16(x), round_bf16(w)

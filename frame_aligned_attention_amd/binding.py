@@ -100,6 +100,12 @@ def _load():
         "fa_stream_seek": ([P, C.c_int32, C.c_int32], C.c_int),
         "fa_stream_set_refs": ([P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
         "fa_stream_destroy": ([P], C.c_int),
+        "fa_w8a8_quantize_act": ([P, C.c_int64, C.c_int32, C.c_int32, P, C.c_int64, P, C.c_int64,
+                                  P], C.c_int),
+        "fa_w8a8_quantize_weight": ([P, C.c_int64, C.c_int32, C.c_int32, P, C.c_int64, P, P],
+                                    C.c_int),
+        "fa_w8a8_gemm": ([P, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int32, C.c_int32,
+                          C.c_int32, P, C.c_int64, P], C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -285,3 +291,32 @@ class Stream:
 
 def fa_stream_create(desc: fa_layout_desc) -> Stream:
     return Stream(desc)
+
+
+# ---------------------------------------------------------------- per-block W8A8 linear layer
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def fa_w8a8_quantize_act(x, xq, sx, stream=None):
+    """x bf16 [m, k] (row-major, rows may be padded) -> xq int8 [m, k], sx fp32 [k/128, ld_sx]."""
+    m, k = x.shape
+    _check(lib.fa_w8a8_quantize_act(_ptr(x), x.stride(0), m, k, _ptr(xq), xq.stride(0), _ptr(sx),
+                                    sx.stride(0), _stream_handle(stream)), "fa_w8a8_quantize_act")
+
+
+def fa_w8a8_quantize_weight(w, wq, sw, stream=None):
+    """w bf16 [n, k] -> wq int8 [n, k], sw fp32 [n/128, k/128]."""
+    n, k = w.shape
+    _check(lib.fa_w8a8_quantize_weight(_ptr(w), w.stride(0), n, k, _ptr(wq), wq.stride(0),
+                                       _ptr(sw), _stream_handle(stream)), "fa_w8a8_quantize_weight")
+
+
+def fa_w8a8_gemm(xq, sx, wq, sw, y, stream=None):
+    """y bf16 [m, n] = W8A8 product of xq [m, k] / sx [k/128, ld_sx] and wq [n, k] / sw."""
+    m, k = xq.shape
+    n = wq.shape[0]
+    _check(lib.fa_w8a8_gemm(_ptr(xq), xq.stride(0), _ptr(sx), sx.stride(0), _ptr(wq), wq.stride(0),
+                            _ptr(sw), m, n, k, _ptr(y), y.stride(0), _stream_handle(stream)),
+           "fa_w8a8_gemm")

@@ -125,4 +125,34 @@ struct QuantArgs {
 
 hipError_t launch_quant_lowbit(const QuantArgs &a, bool mean_given, hipStream_t s);
 
+// Per-block W8A8 linear layer.  Quantiser: bf16 [rows][ld_in] -> int8 [rows][ld_out]; scales
+// per (row, 128-column block) at scale[block * ld_scale + row] (activations) or per 128 x 128
+// block at scale[row_block * (cols/128) + block] (weights).
+struct W8QuantArgs {
+  const void *in;
+  int64_t ld_in;   // elements
+  void *out;
+  int64_t ld_out;  // bytes
+  float *scale;
+  int64_t ld_scale;
+  int32_t rows, cols;
+};
+
+// y [m][ld_y] bf16 = dequant(xq [m][ld_xq] int8, sx [k/128][ld_sx]) . dequant(wq [n][ld_wq] int8,
+// sw [n/128][k/128])^T; n and k multiples of 128.
+struct W8GemmArgs {
+  const void *xq;
+  const float *sx;
+  const void *wq;
+  const float *sw;
+  void *y;
+  int64_t ld_xq, ld_wq, ld_y;
+  int32_t ld_sx;
+  int32_t m, n, k;
+};
+
+hipError_t launch_w8a8_quant_act(const W8QuantArgs &a, hipStream_t s);
+hipError_t launch_w8a8_quant_weight(const W8QuantArgs &a, hipStream_t s);
+hipError_t launch_w8a8_gemm(const W8GemmArgs &a, hipStream_t s);
+
 }  // namespace fa

@@ -1,0 +1,286 @@
+// fa_w8a8.hip -- per-block W8A8 linear layer for gfx950: y = x . w^T with int8 activations
+// (one fp32 scale per row and 128-column block) and int8 weights (one fp32 scale per 128 x 128
+// block), as the tech report's paragraph on linear layers describes (fine-grained block scales
+// keep an outlier from setting the range of a whole tensor or channel).
+//
+// Quantisers: scale = absmax/127, code = round_half_even(x * (127/absmax)) clamped to +-127,
+// the same arithmetic as the attention path's quantiser.
+//
+// GEMM.  One workgroup (4 waves) per 128 (n) x 128 (m) output tile.  Every 128-column K-block
+// is one quantisation block: the int32 products of its four 32-deep k-steps accumulate in the
+// MFMA (v_mfma_i32_32x32x32_i8, exact), then are dequantised into fp32 accumulators with the
+// block's two scales.  The product is computed as y^T = w . x^T (weights as the A operand), so
+// each lane's output column is one activation row: the activation scale is one register per
+// 32-row tile and the weight scale is uniform per workgroup.  Operand tiles go straight from
+// HBM into double-buffered LDS (direct loads, bounds-checked descriptors zero-fill rows past
+// m), rows XOR-swizzled in 16-byte chunks for conflict-free MFMA operand reads.
+#include "fa_device.h"
+
+namespace fa {
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// ============================================================== quantisers
+
+// Activations: 16 lanes per (row, 128-column block), 8 values each; 16 blocks per workgroup.
+__global__ void __launch_bounds__(256) w8a8_quant_act_kernel(const W8QuantArgs a) {
+  const int grp = blockIdx.x * 16 + (threadIdx.x >> 4), l16 = threadIdx.x & 15;
+  const int kbt = a.cols / 128;
+  const int row = grp / kbt, kb = grp - (grp / kbt) * kbt;
+  if (row >= a.rows) return;  // whole 16-lane groups leave together
+  const bf16x8_t v =
+      *(const bf16x8_t *)((const __bf16 *)a.in + (int64_t)row * a.ld_in + kb * 128 + l16 * 8);
+  float x[8], amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = (float)v[i];
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  uint32_t w32[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = fminf(fmaxf(__builtin_rintf(x[4 * k + i] * inv), -127.0f), 127.0f);
+      u |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+    }
+    w32[k] = u;
+  }
+  *(uint2 *)((int8_t *)a.out + (int64_t)row * a.ld_out + kb * 128 + l16 * 8) = uint2{w32[0], w32[1]};
+  if (l16 == 0) a.scale[(int64_t)kb * a.ld_scale + row] = amax / 127.0f;
+}
+
+// Weights: one workgroup per 128 x 128 block; thread t covers half a row (64 values).
+__global__ void __launch_bounds__(256) w8a8_quant_weight_kernel(const W8QuantArgs a) {
+  const int kbt = a.cols / 128;
+  const int nb = blockIdx.x / kbt, kb = blockIdx.x - (blockIdx.x / kbt) * kbt;
+  const int t = threadIdx.x, row = nb * 128 + (t >> 1), c0 = kb * 128 + (t & 1) * 64;
+  const __bf16 *p = (const __bf16 *)a.in + (int64_t)row * a.ld_in + c0;
+  float x[64], amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16x8_t v = *(const bf16x8_t *)(p + 8 * j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[8 * j + i] = (float)v[i];
+      amax = fmaxf(amax, fabsf(x[8 * j + i]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  __shared__ float red[4];
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  int8_t *o = (int8_t *)a.out + (int64_t)row * a.ld_out + c0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w32[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t u = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r = fminf(fmaxf(__builtin_rintf(x[16 * j + 4 * k + i] * inv), -127.0f), 127.0f);
+        u |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+      }
+      w32[k] = u;
+    }
+    *(uint4 *)(o + 16 * j) = uint4{w32[0], w32[1], w32[2], w32[3]};
+  }
+  if (t == 0) a.scale[(int64_t)nb * kbt + kb] = amax / 127.0f;
+}
+
+// ============================================================== GEMM
+
+namespace w8 {
+constexpr int BM = 128, BN = 128, BK = 128;  // output tile (m, n); K-block = quantisation block
+constexpr int TILEB = 128 * BK;             // bytes of one operand tile (128 rows x 128 int8)
+constexpr int LOADS = TILEB / (256 * 16);   // 16-byte direct loads per thread per operand tile
+constexpr int RSTEP = 256 * 16 / BK;        // rows covered by one load of all lanes (32)
+// chunk c of row r lives at chunk c ^ ((r >> 1) & 7): a ds_read_b128 of 16 lanes (16 rows at
+// one logical chunk) then touches 16 distinct (row parity, chunk) bank groups
+__device__ __forceinline__ int sw(int r) { return (r >> 1) & 7; }
+}  // namespace w8
+
+__global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
+  using namespace w8;
+  __shared__ __attribute__((aligned(1024))) char xb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char xb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char wb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char wb1[TILEB];
+
+  // Work item: slot j*8 + x runs on XCD x; each XCD takes a contiguous run of (n tile, m tile)
+  // items in n-major order, so the workgroups an XCD runs together share a weight tile in L2.
+  const int mt_count = (a.m + BM - 1) / BM, nt_count = a.n / BN;
+  const int total = mt_count * nt_count, per = (total + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= total) return;
+  const int nt = item / mt_count, mt = item - (item / mt_count) * mt_count;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int kbt = a.k / BK;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wn = wave >> 1, wm = wave & 1;  // wave's 64 x 64 corner: n rows wn*64.., m rows wm*64..
+
+  // direct loads: load j of wave w fills LDS chunks (4j + w)*64 + lane = row row0 + j*RSTEP,
+  // logical chunk lc (the swizzle is the same for every j since RSTEP is a multiple of 16)
+  const int p0 = wave * 64 + lane;
+  const int lrow0 = p0 / 8;
+  const int lcol = ((p0 % 8) ^ sw(lrow0)) * 16;
+  const uint32_t xoff0 = (uint32_t)lrow0 * (uint32_t)a.ld_xq + lcol;
+  const uint32_t woff0 = (uint32_t)lrow0 * (uint32_t)a.ld_wq + lcol;
+  const int xrows = min(BM, a.m - m0);
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc((uint64_t)a.xq + (uint64_t)m0 * a.ld_xq, (int)((int64_t)xrows * a.ld_xq));
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc((uint64_t)a.wq + (uint64_t)n0 * a.ld_wq, (int)((int64_t)BN * a.ld_wq));
+  auto issue = [&](int kb, char *xdst, char *wdst) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      lds_char *dx = (lds_char *)xdst + (4 * j + wave) * 1024;
+      lds_char *dw = (lds_char *)wdst + (4 * j + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void *)dx, 16,
+          (int)(xoff0 + (uint32_t)(j * RSTEP) * (uint32_t)a.ld_xq + kb * BK), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void *)dw, 16,
+          (int)(woff0 + (uint32_t)(j * RSTEP) * (uint32_t)a.ld_wq + kb * BK), 0, 0, 0);
+    }
+  };
+
+  // operand reads: lane reads row (tile base + l32), logical chunk 2*ks + hl of the K-block
+  int coff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) coff[ks] = (((2 * ks + hl) ^ sw(l32)) * 16);
+
+  // activation scales: lane's row is m0 + wm*64 + tm*32 + l32; rows past m read 0 (bounds)
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc((uint64_t)a.sx, (int)((int64_t)kbt * a.ld_sx * 4));
+  auto load_sx = [&](int kb, float (&s)[2]) {
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = m0 + wm * 64 + tm * 32 + l32;
+      s[tm] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(srs, (kb * a.ld_sx + row) * 4, 0, 0));
+    }
+  };
+  const cFloat *swp = (const cFloat *)a.sw + (int64_t)nt * kbt;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) acc[tn][tm] = f32x16_t{};
+
+  auto compute = [&](const char *xbuf, const char *wbuf, const float (&sx)[2], float swk) {
+    const lds_char *X = (const lds_char *)xbuf, *W = (const lds_char *)wbuf;
+    i32x16_t part[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      i32x4_t wf[2], xf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        wf[t] = *(const i32x4_t *)(W + (wn * 64 + t * 32 + l32) * BK + coff[ks]);
+        xf[t] = *(const i32x4_t *)(X + (wm * 64 + t * 32 + l32) * BK + coff[ks]);
+      }
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+          part[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              wf[tn], xf[tm], ks == 0 ? i32x16_t{} : part[tn][tm], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const float s = sx[tm] * swk;
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tn][tm][i] = fmaf((float)part[tn][tm][i], s, acc[tn][tm][i]);
+    }
+  };
+  auto sync = [&]() {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  float sxa[2], sxb[2];
+  issue(0, xb0, wb0);
+  load_sx(0, sxa);
+  sync();
+  int kb = 0;
+  while (true) {
+    // even K-block in buffers 0, next into buffers 1
+    if (kb + 1 < kbt) {
+      issue(kb + 1, xb1, wb1);
+      load_sx(kb + 1, sxb);
+    }
+    compute(xb0, wb0, sxa, swp[kb]);
+    sync();
+    if (++kb >= kbt) break;
+    if (kb + 1 < kbt) {
+      issue(kb + 1, xb0, wb0);
+      load_sx(kb + 1, sxa);
+    }
+    compute(xb1, wb1, sxb, swp[kb]);
+    sync();
+    if (++kb >= kbt) break;
+  }
+
+  // epilogue: y[m][n] bf16; lane's m = m0 + wm*64 + tm*32 + l32, n = n0 + wn*64 + tn*32 +
+  // (i/4)*8 + 4*hl + i%4 (four consecutive columns per group of four accumulator registers)
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm) {
+    const int row = m0 + wm * 64 + tm * 32 + l32;
+    if (row >= a.m) continue;
+    __bf16 *yr = (__bf16 *)a.y + (int64_t)row * a.ld_y + n0 + wn * 64 + 4 * hl;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)acc[tn][tm][4 * g + i];
+        *(bf16x4_t *)(yr + tn * 32 + g * 8) = v;
+      }
+  }
+}
+
+hipError_t launch_w8a8_quant_act(const W8QuantArgs &a, hipStream_t s) {
+  const int64_t groups = (int64_t)a.rows * (a.cols / 128);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(w8a8_quant_act_kernel, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_w8a8_quant_weight(const W8QuantArgs &a, hipStream_t s) {
+  const int blocks = (a.rows / 128) * (a.cols / 128);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(w8a8_quant_weight_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_w8a8_gemm(const W8GemmArgs &a, hipStream_t s) {
+  const int total = ((a.m + 127) / 128) * (a.n / 128);
+  if (total == 0) return hipSuccess;
+  const int per = (total + 7) / 8;
+  hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(per * 8), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

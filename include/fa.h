@@ -246,6 +246,38 @@ fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const
                          int32_t frames, fa_hip_stream stream);
 
 /*
+ * Per-block W8A8 linear layer (tech report, paragraph on linear layers: a
+ * per-block W8A8 GEMM whose fine-grained scales keep an outlier from setting
+ * the range of a whole tensor or channel; the launch article's technical-stack
+ * section names it beside the attention work).  The projections either side
+ * of the attention: y = x . w^T.  int8 codes with one fp32 scale per block:
+ * activations per (row, 128-column block), weights per 128 x 128 block;
+ * scale = absmax/127, code = round_half_even(x * (127/absmax)) clamped to
+ * +-127.  All matrices row-major with K (the reduction dimension) contiguous;
+ * ld_* are leading dimensions in elements.  The caller owns every buffer; all
+ * calls are asynchronous on `stream` and allocate nothing.  Argument errors
+ * (NULL, misaligned base or rows -- bases 16-byte aligned, rows a multiple of
+ * 16 bytes --, k or n not multiples of 128, ld < columns) return
+ * FA_ERR_INVALID before any launch; FA_ERR_HIP on a failed launch.
+ *
+ * fa_w8a8_quantize_act: x bf16 [m][ld_x] -> xq int8 [m][ld_xq] and sx fp32
+ * with the scale of row i, K-block b at sx[b * ld_sx + i] (ld_sx >= m).
+ * m may be any size (0 is a no-op); k a multiple of 128.
+ */
+fa_status fa_w8a8_quantize_act(const void *x, int64_t ld_x, int32_t m, int32_t k, int8_t *xq,
+                               int64_t ld_xq, float *sx, int64_t ld_sx, fa_hip_stream stream);
+/* fa_w8a8_quantize_weight: w bf16 [n][ld_w] -> wq int8 [n][ld_wq] and sw fp32
+ * [n/128][k/128] row-major; n and k multiples of 128 (done once per weight). */
+fa_status fa_w8a8_quantize_weight(const void *w, int64_t ld_w, int32_t n, int32_t k, int8_t *wq,
+                                  int64_t ld_wq, float *sw, fa_hip_stream stream);
+/* fa_w8a8_gemm: y bf16 [m][ld_y] = sum over K-blocks b of sx[b][i] * sw[j/128][b] *
+ * (exact int32 dot of the block), accumulated in fp32, rounded to bf16 once.
+ * n and k multiples of 128, m any size. */
+fa_status fa_w8a8_gemm(const int8_t *xq, int64_t ld_xq, const float *sx, int64_t ld_sx,
+                       const int8_t *wq, int64_t ld_wq, const float *sw, int32_t m, int32_t n,
+                       int32_t k, void *y, int64_t ld_y, fa_hip_stream stream);
+
+/*
  * Streaming driver: one object per stream of chunks.  It keeps the frame
  * counter and what the ring holds, caches the layout of every distinct
  * chunk position, and per chunk runs attention over (ring history in the
