@@ -9,7 +9,8 @@
 // GEMM.  One workgroup (4 waves) per 128 (n) x 128 (m) output tile.  Every 128-column K-block
 // is one quantisation block: the int32 products of its four 32-deep k-steps accumulate in the
 // MFMA (v_mfma_i32_32x32x32_i8, exact), then are dequantised into fp32 accumulators with the
-// block's two scales.  The product is computed as y^T = w . x^T (weights as the A operand), so
+// block's two scales -- one K-block later, beside the next block's MFMAs.  The product is
+// computed as y^T = w . x^T (weights as the A operand), so
 // each lane's output column is one activation row: the activation scale is one register per
 // 32-row tile and the weight scale is uniform per workgroup.  Operand tiles go straight from
 // HBM into double-buffered LDS (direct loads, bounds-checked descriptors zero-fill rows past
@@ -105,6 +106,40 @@ __global__ void __launch_bounds__(256) w8a8_quant_weight_kernel(const W8QuantArg
 
 // ============================================================== GEMM
 
+// Grid slot -> (m tile, n tile).  Workgroups are handed to the 8 XCDs round robin (slot j*8 + x
+// runs on XCD x).  With 8 or more n tiles, XCD x owns the n tiles [x*NT/8, (x+1)*NT/8) and walks
+// them in groups of 8 m tiles: the ~64 workgroups an XCD runs at once then cover about 8 m tiles
+// x 8 n tiles, so each K-block slice of an activation or weight tile is read from HBM or the
+// last-level cache once and reused about 8 times from the XCD's L2.  Fewer n tiles: plain order.
+__host__ __device__ inline int w8a8_grid(int mt_count, int nt_count) {
+  if (nt_count < 8) return mt_count * nt_count;
+  return 8 * ((nt_count + 7) / 8) * mt_count;
+}
+__device__ inline bool w8a8_item(int slot, int mt_count, int nt_count, int &mt, int &nt) {
+  if (nt_count < 8) {
+    if (slot >= mt_count * nt_count) return false;
+    mt = slot / nt_count;
+    nt = slot - mt * nt_count;
+    return true;
+  }
+  const int x = slot % 8, j = slot / 8;
+  const int nt_lo = x * nt_count / 8, ntx = (x + 1) * nt_count / 8 - nt_lo;
+  if (j >= ntx * mt_count) return false;
+  const int full = (mt_count / 8) * 8;  // m tiles in complete groups of 8
+  int ntl;
+  if (j < full * ntx) {
+    const int g = j / (8 * ntx), r = j - g * (8 * ntx);
+    ntl = r / 8;
+    mt = g * 8 + (r % 8);
+  } else {
+    const int r = j - full * ntx, rem = mt_count - full;
+    ntl = r / rem;
+    mt = full + (r % rem);
+  }
+  nt = nt_lo + ntl;
+  return true;
+}
+
 namespace w8 {
 constexpr int BM = 128, BN = 128, BK = 128;  // output tile (m, n); K-block = quantisation block
 constexpr int TILEB = 128 * BK;             // bytes of one operand tile (128 rows x 128 int8)
@@ -122,13 +157,9 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char wb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char wb1[TILEB];
 
-  // Work item: slot j*8 + x runs on XCD x; each XCD takes a contiguous run of (n tile, m tile)
-  // items in n-major order, so the workgroups an XCD runs together share a weight tile in L2.
   const int mt_count = (a.m + BM - 1) / BM, nt_count = a.n / BN;
-  const int total = mt_count * nt_count, per = (total + 7) / 8;
-  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (item >= total) return;
-  const int nt = item / mt_count, mt = item - (item / mt_count) * mt_count;
+  int mt, nt;
+  if (!w8a8_item((int)blockIdx.x, mt_count, nt_count, mt, nt)) return;
   const int m0 = mt * BM, n0 = nt * BN;
   const int kbt = a.k / BK;
 
@@ -187,9 +218,9 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm) acc[tn][tm] = f32x16_t{};
 
-  auto compute = [&](const char *xbuf, const char *wbuf, const float (&sx)[2], float swk) {
+  // the 16 MFMAs of one K-block: int32 products of its four 32-deep k-steps, per 32x32 tile
+  auto mfmas = [&](const char *xbuf, const char *wbuf, i32x16_t (&part)[2][2]) {
     const lds_char *X = (const lds_char *)xbuf, *W = (const lds_char *)wbuf;
-    i32x16_t part[2][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       i32x4_t wf[2], xf[2];
@@ -205,6 +236,9 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
           part[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
               wf[tn], xf[tm], ks == 0 ? i32x16_t{} : part[tn][tm], 0, 0, 0);
     }
+  };
+  // fold one K-block's products into the fp32 accumulators with its two scales
+  auto dequant = [&](const i32x16_t (&part)[2][2], const float (&sx)[2], float swk) {
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm) {
       const float s = sx[tm] * swk;
@@ -214,32 +248,51 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
         for (int i = 0; i < 16; ++i) acc[tn][tm][i] = fmaf((float)part[tn][tm][i], s, acc[tn][tm][i]);
     }
   };
+  // One pipeline step: the MFMAs of K-block kb (tiles in xbuf / wbuf) into pn while the
+  // products of block kb-1 (pp, scales sx and swk) are dequantised; the two are independent,
+  // so the schedule puts the dequantisation beside the MFMAs.
+  auto step = [&](const char *xbuf, const char *wbuf, i32x16_t (&pn)[2][2],
+                  const i32x16_t (&pp)[2][2], const float (&sx)[2], float swk) {
+    mfmas(xbuf, wbuf, pn);
+    dequant(pp, sx, swk);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS: operands of k-step 0
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i % 4 == 0 && i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS
+      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (prefetch)
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU (dequantisation)
+    }
+  };
   auto sync = [&]() {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
+  // K-block kb's tiles sit in buffers kb % 2; its products are dequantised one step later.  A
+  // last drain step (kb == kbt) dequantises the final block; its MFMAs read whatever the buffer
+  // holds and their products are dropped (int8 products cannot be NaN).
   float sxa[2], sxb[2];
+  i32x16_t pa[2][2], pb[2][2];
   issue(0, xb0, wb0);
   load_sx(0, sxa);
   sync();
-  int kb = 0;
-  while (true) {
-    // even K-block in buffers 0, next into buffers 1
-    if (kb + 1 < kbt) {
-      issue(kb + 1, xb1, wb1);
-      load_sx(kb + 1, sxb);
-    }
-    compute(xb0, wb0, sxa, swp[kb]);
+  if (kbt > 1) issue(1, xb1, wb1);
+  mfmas(xb0, wb0, pa);
+  sync();
+  for (int kb = 1;;) {
+    // odd kb: tiles in buffers 1, products into pb; block kb-1 in pa / sxa
+    if (kb + 1 < kbt) issue(kb + 1, xb0, wb0);
+    if (kb < kbt) load_sx(kb, sxb);
+    step(xb1, wb1, pb, pa, sxa, swp[kb - 1]);
     sync();
-    if (++kb >= kbt) break;
-    if (kb + 1 < kbt) {
-      issue(kb + 1, xb0, wb0);
-      load_sx(kb + 1, sxa);
-    }
-    compute(xb1, wb1, sxb, swp[kb]);
+    if (++kb > kbt) break;
+    // even kb: tiles in buffers 0, products into pa; block kb-1 in pb / sxb
+    if (kb + 1 < kbt) issue(kb + 1, xb1, wb1);
+    if (kb < kbt) load_sx(kb, sxa);
+    step(xb0, wb0, pa, pb, sxb, swp[kb - 1]);
     sync();
-    if (++kb >= kbt) break;
+    if (++kb > kbt) break;
   }
 
   // epilogue: y[m][n] bf16; lane's m = m0 + wm*64 + tm*32 + l32, n = n0 + wn*64 + tn*32 +
@@ -276,10 +329,9 @@ hipError_t launch_w8a8_quant_weight(const W8QuantArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_w8a8_gemm(const W8GemmArgs &a, hipStream_t s) {
-  const int total = ((a.m + 127) / 128) * (a.n / 128);
-  if (total == 0) return hipSuccess;
-  const int per = (total + 7) / 8;
-  hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(per * 8), dim3(256), 0, s, a);
+  const int grid = w8a8_grid((a.m + 127) / 128, a.n / 128);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
