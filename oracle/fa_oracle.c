@@ -325,6 +325,34 @@ void fa_oracle_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, co
     }
 }
 
+void fa_oracle_norm_rope(const float *x, int N, int H, int D, const float *gamma, double eps,
+                         const int *pos, double base, float *out) {
+  const int P = D / 2, py = D / 6, pt = P - 2 * py;
+  const int gsize[3] = {pt, py, py}, gstart[3] = {0, pt, pt + py};
+  int n, h;
+#pragma omp parallel for private(h) schedule(static)
+  for (n = 0; n < N; ++n)
+    for (h = 0; h < H; ++h) {
+      const float *xv = x + ((long)n * H + h) * D;
+      float *ov = out + ((long)n * H + h) * D;
+      double ss = 0.0, y[1024];
+      int d, g, j;
+      for (d = 0; d < D; ++d) ss += (double)xv[d] * (double)xv[d];
+      {
+        const double r = sqrt(ss / D + eps);
+        for (d = 0; d < D; ++d) y[d] = (double)xv[d] / r * (double)gamma[d];
+      }
+      for (g = 0; g < 3; ++g)
+        for (j = 0; j < gsize[g]; ++j) {
+          const int i = gstart[g] + j;
+          const double ang = (double)pos[n * 3 + g] * pow(base, -(double)j / gsize[g]);
+          const double a = y[i], b = y[i + P];
+          ov[i] = (float)(a * cos(ang) - b * sin(ang));
+          ov[i + P] = (float)(a * sin(ang) + b * cos(ang));
+        }
+    }
+}
+
 /* OCP e4m3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits.  Normal
  * values 2^(e-7) * (1 + m/8) for e = 1..15 (except e=15,m=7 which is NaN),
  * subnormals 2^-6 * m/8.  Largest finite 448.  Encoding here: round to the

@@ -132,6 +132,21 @@ void fa_oracle_quant_int8_2d(const float *x, int rows, int cols, int br, int bc,
 void fa_oracle_w8a8_gemm(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
                          int m, int n, int k, double *y);
 
+/*
+ * QK prologue: RMSNorm then rotary position embedding, per (token, head).  The
+ * tech report's kernel-fusion paragraph fuses RMSNorm with elementwise work,
+ * and the structured summary gives each token stream condition-specific RoPE
+ * positions; neither gives formulas, so this is a stated reading:
+ *   RMSNorm: y = x / sqrt(mean_d x^2 + eps) * gamma[d]   (gamma [D], all heads)
+ *   RoPE over three axes (t, y, x): the D/2 rotation pairs (d, d + D/2) are
+ *   split into groups of pt = D/2 - 2*floor(D/6), py = px = floor(D/6) pairs
+ *   (t first); pair j of a group of g pairs turns by angle pos_axis * base^(-j/g):
+ *   (a, b) -> (a cos - b sin, a sin + b cos) with a = y[d], b = y[d + D/2].
+ * x, out [N][H][D]; pos [N][3] (t, y, x) per token; double arithmetic.
+ */
+void fa_oracle_norm_rope(const float *x, int N, int H, int D, const float *gamma, double eps,
+                         const int *pos, double base, float *out);
+
 /* OCP e4m3 (bias 7, no infinities, 0x7f/0xff NaN, max 448): RNE, saturating. */
 uint8_t fa_oracle_e4m3_encode(float x);
 float fa_oracle_e4m3_decode(uint8_t c);

@@ -67,6 +67,8 @@ def _bind(path: str):
     i8p = C.POINTER(C.c_int8)
     lib.fa_oracle_w8a8_gemm.argtypes = [i8p, fp, i8p, fp, C.c_int, C.c_int, C.c_int,
                                         C.POINTER(C.c_double)]
+    lib.fa_oracle_norm_rope.argtypes = [fp, C.c_int, C.c_int, C.c_int, fp, C.c_double, ip,
+                                        C.c_double, fp]
     return lib
 
 
@@ -279,3 +281,17 @@ def w8a8_gemm(xq, sx, wq, sw, lib=None):
     lib.fa_oracle_w8a8_gemm(xq.ctypes.data_as(i8p), _fp(sx), wq.ctypes.data_as(i8p), _fp(sw),
                             m, n, k, y.ctypes.data_as(C.POINTER(C.c_double)))
     return y
+
+
+def norm_rope(x, gamma, eps, pos, base=10000.0, lib=None):
+    """QK-RMSNorm + three-axis RoPE: x [N,H,D] fp32, gamma [D], pos [N,3] int -> [N,H,D]."""
+    lib = lib or load()
+    x = _f32(x)
+    N, H, D = x.shape
+    assert D <= 1024 and D % 2 == 0
+    g = _f32(gamma)
+    p = np.ascontiguousarray(pos, np.int32)
+    out = np.zeros_like(x)
+    lib.fa_oracle_norm_rope(_fp(x), N, H, D, _fp(g), float(eps),
+                            p.ctypes.data_as(C.POINTER(C.c_int)), float(base), _fp(out))
+    return out

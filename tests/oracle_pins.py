@@ -23,6 +23,8 @@ What pins what:
   quantiser         hand-derived codes, round-trip bound, torch float8_e4m3fn
   W8A8              hand-derived block codes, torch round; integer matmul (numpy), per-block
                     scale weighting, closed-form quantisation error bound
+  norm + RoPE       numpy RMSNorm at position 0, norm kept, relative positions, hand-derived
+                    single-pair rotations on each axis
 """
 from __future__ import annotations
 
@@ -595,7 +597,54 @@ def pin_w8a8_gemm(lib):
     assert np.abs(y - exact).max() > 0  # the quantisation did something
 
 
+def pin_norm_rope(lib):
+    """QK-RMSNorm + three-axis RoPE (a stated reading): zero positions give the textbook RMSNorm
+    (numpy), the rotation keeps each vector's norm, dot products depend only on position
+    differences along every axis, and hand-derived single-pair rotations."""
+    g = np.random.default_rng(8)
+    N, H, D = 5, 2, 12
+    x = g.standard_normal((N, H, D)).astype(np.float32)
+    gamma = g.uniform(0.5, 1.5, D).astype(np.float32)
+    eps = 1e-2
+    z = np.zeros((N, 3), np.int32)
+    out = O.norm_rope(x, gamma, eps, z, lib=lib)
+    x64 = x.astype(np.float64)
+    want = x64 / np.sqrt((x64 ** 2).mean(-1, keepdims=True) + eps) * gamma.astype(np.float64)
+    close(out, want, 1e-6, "RoPE at position 0 is the plain RMSNorm")
+    pos = g.integers(0, 50, size=(N, 3)).astype(np.int32)
+    rot = O.norm_rope(x, gamma, eps, pos, lib=lib)
+    close(np.linalg.norm(rot.astype(np.float64), axis=-1), np.linalg.norm(want, axis=-1), 1e-6,
+          "rotation keeps the norm")
+    # <rope(q, p), rope(k, p')> depends on p - p' only
+    q = g.standard_normal((2, 1, 128)).astype(np.float32)
+    one = np.ones(128, np.float32)
+    for axis in range(3):
+        dots = []
+        for shift in (0, 7, 300):
+            pp = np.zeros((2, 3), np.int32)
+            pp[0, axis], pp[1, axis] = 11 + shift, 4 + shift
+            r = O.norm_rope(q, one, 0.0, pp, lib=lib).astype(np.float64)
+            dots.append(float(r[0, 0] @ r[1, 0]))
+        close(dots[1:], [dots[0]] * 2, 1e-5, "relative position along axis %d" % axis)
+    # D = 12: pairs (d, d+6); t pairs 0, 1; y pairs 2, 3; x pairs 4, 5; theta_j = 1e4^(-j/2)
+    def single(ch, p3):
+        v = np.zeros((1, 1, 12), np.float32)
+        v[0, 0, ch] = 1.0
+        return O.norm_rope(v, np.ones(12, np.float32), 0.0, np.array([p3], np.int32), lib=lib)[0, 0]
+    r12 = np.sqrt(12.0)
+    e = np.zeros(12)
+    e[1], e[7] = r12 * np.cos(0.03), r12 * np.sin(0.03)    # t axis, pair j=1, t=3
+    close(single(1, (3, 0, 0)), e, 1e-6, "t-axis pair")
+    e = np.zeros(12)
+    e[3], e[9] = r12 * np.cos(0.05), r12 * np.sin(0.05)    # y axis, pair j=1, y=5
+    close(single(3, (0, 5, 0)), e, 1e-6, "y-axis pair")
+    e = np.zeros(12)
+    e[4], e[10] = -r12 * np.sin(2.0), r12 * np.cos(2.0)    # x axis, pair j=0 (second half), x=2
+    close(single(10, (0, 0, 2)), e, 1e-6, "x-axis pair")
+
+
 ALL_PINS = [pin_golden_masks, pin_bruteforce, pin_f1_full_attention, pin_two_keys,
             pin_large_scores, pin_q_zero,
             pin_ones_v, pin_perturbations, pin_permutation, pin_split_merge,
-            pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean, pin_w8a8_quant, pin_w8a8_gemm]
+            pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean, pin_w8a8_quant, pin_w8a8_gemm,
+            pin_norm_rope]

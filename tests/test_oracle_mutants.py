@@ -53,6 +53,14 @@ MUTANTS = {
     "w8a8 activation scale dropped": ("acc += (double)sx[(long)i * kb + b] * ", "acc += "),
     "w8a8 block of 64": ("int t1 = (b + 1) * 128 < k ? (b + 1) * 128 : k;",
                          "int t1 = (b + 1) * 128 - 64 < k ? (b + 1) * 128 - 64 : k;"),
+    "rope partner off by one": ("const double a = y[i], b = y[i + P];",
+                                "const double a = y[i], b = y[(i + P + 1) % D];"),
+    "rope frequency exponent doubled": ("pow(base, -(double)j / gsize[g])",
+                                        "pow(base, -2.0 * (double)j / gsize[g])"),
+    "rmsnorm eps dropped": ("const double r = sqrt(ss / D + eps);", "const double r = sqrt(ss / D);"),
+    "rmsnorm gamma dropped": ("y[d] = (double)xv[d] / r * (double)gamma[d];",
+                              "y[d] = (double)xv[d] / r;"),
+    "rope axes swapped": ("(double)pos[n * 3 + g]", "(double)pos[n * 3 + (g + 1) % 3]"),
     "kmean off by one": ("mean[h * D + d] = n ? (float)(acc / (double)n) : 0.0f;",
                          "mean[h * D + d] = n ? (float)(acc / (double)(n + 1)) : 0.0f;"),
 }
