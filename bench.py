@@ -359,6 +359,42 @@ def time_w8a8(torch, W, B, reps=10):
             "torch_bf16_mm_ms": round(bf_ms, 4)}
 
 
+def time_prologue(torch, W, B, reps=10):
+    """QK prologue on the queries of one chunk of the 1560-token 40-head stream (target and
+    source tokens: 9,360 x 40 heads x 128): RMSNorm + RoPE bf16 -> bf16, and fused with the
+    low-bit quantiser (-> int8 + block scales); HBM bytes moved against 8 TB/s."""
+    n, H, D = 9360, 40, 128
+    g = torch.Generator().manual_seed(0)
+    x = torch.randn((1, n, H, D), generator=g).to(torch.bfloat16).to("cuda")
+    gamma = torch.ones(D, device="cuda")
+    p = torch.arange(n)
+    pos = torch.stack([57 + (p % 4680) // 1560, (p % 1560) // 52, p % 52], 1).to(torch.int32).cuda()
+    y = torch.empty_like(x)
+    codes = torch.empty((1, n, H, D), dtype=torch.int8, device="cuda")
+    scales = torch.empty((1, H, (n + 127) // 128), dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return statistics.median([e[0].elapsed_time(e[1]) for e in ev])
+
+    t_nr = timed(lambda: B.fa_qk_norm_rope(x, y, gamma, pos))
+    t_q = timed(lambda: B.fa_qk_norm_rope_quant(x, codes, scales, gamma, pos, False))
+    nb = n * H * D * 2
+    return {"workload": "qk-prologue-9360x40x128 (queries of a 1560-token 40-head chunk)",
+            "norm_rope_ms": round(t_nr, 4), "norm_rope_gbs": round(2 * nb / t_nr / 1e6, 1),
+            "norm_rope_quant_ms": round(t_q, 4),
+            "norm_rope_quant_gbs": round(1.5 * nb / t_q / 1e6, 1),
+            "hbm_frac": round(2 * nb / t_nr / 1e6 / 8000.0, 3)}
+
+
 def cpu_baseline(W, budget_s):
     """The oracle, as it stands, on a bounded sample of the steady chunk (chunk 19)."""
     import numpy as np
@@ -555,7 +591,8 @@ def main():
                                   time_single_call(2, torch, W, B, sink=3),
                                   time_graph_chunk(torch, W, B, False),
                                   time_graph_chunk(torch, W, B, True),
-                                  time_w8a8(torch, W, B)]
+                                  time_w8a8(torch, W, B),
+                                  time_prologue(torch, W, B)]
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (%.0f s budget)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)

@@ -100,6 +100,11 @@ def _load():
         "fa_stream_seek": ([P, C.c_int32, C.c_int32], C.c_int),
         "fa_stream_set_refs": ([P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
         "fa_stream_destroy": ([P], C.c_int),
+        "fa_qk_norm_rope": ([C.POINTER(fa_tensor), C.POINTER(fa_tensor), P, C.c_float, P,
+                             C.c_float, C.c_int32, C.c_int32, C.c_int32, C.c_int32, P], C.c_int),
+        "fa_qk_norm_rope_quant": ([C.POINTER(fa_tensor), C.POINTER(fa_tensor), P, C.c_float, P,
+                                   C.c_float, C.c_int32, P, P, C.c_float, C.c_int32, C.c_int32,
+                                   C.c_int32, C.c_int32, P], C.c_int),
         "fa_w8a8_quantize_act": ([P, C.c_int64, C.c_int32, C.c_int32, P, C.c_int64, P, C.c_int64,
                                   P], C.c_int),
         "fa_w8a8_quantize_weight": ([P, C.c_int64, C.c_int32, C.c_int32, P, C.c_int64, P, P],
@@ -320,3 +325,26 @@ def fa_w8a8_gemm(xq, sx, wq, sw, y, stream=None):
     _check(lib.fa_w8a8_gemm(_ptr(xq), xq.stride(0), _ptr(sx), sx.stride(0), _ptr(wq), wq.stride(0),
                             _ptr(sw), m, n, k, _ptr(y), y.stride(0), _stream_handle(stream)),
            "fa_w8a8_gemm")
+
+
+# ---------------------------------------------------------------- QK prologue (RMSNorm + RoPE)
+
+def fa_qk_norm_rope(x, out, gamma, pos, eps=1e-6, rope_base=10000.0, stream=None):
+    """x, out bf16 [B, N, H, D] (or [N, H, D]); gamma fp32 [D]; pos int32 [N, 3]."""
+    xs = x if x.dim() == 4 else x.unsqueeze(0)
+    b, n, h, d = xs.shape
+    ti, to = tensor(x), tensor(out)
+    _check(lib.fa_qk_norm_rope(C.byref(ti), C.byref(to), _ptr(gamma), eps, _ptr(pos), rope_base,
+                               n, b, h, d, _stream_handle(stream)), "fa_qk_norm_rope")
+
+
+def fa_qk_norm_rope_quant(x, codes, scales, gamma, pos, is_key, k_mean=None, lse_shift=None,
+                          eps=1e-6, rope_base=10000.0, softmax_scale=0.0, stream=None):
+    """x bf16 [B, N, H, 128] -> codes int8 (same shape) and scales fp32 [B, H, ceil(N/128)]."""
+    xs = x if x.dim() == 4 else x.unsqueeze(0)
+    b, n, h, d = xs.shape
+    ti, tc = tensor(x), tensor(codes, scales)
+    _check(lib.fa_qk_norm_rope_quant(C.byref(ti), C.byref(tc), _ptr(gamma), eps, _ptr(pos),
+                                     rope_base, int(is_key), _ptr(k_mean), _ptr(lse_shift),
+                                     softmax_scale, n, b, h, d, _stream_handle(stream)),
+           "fa_qk_norm_rope_quant")

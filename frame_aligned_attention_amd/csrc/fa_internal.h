@@ -151,6 +151,26 @@ struct W8GemmArgs {
   int32_t m, n, k;
 };
 
+// QK prologue (RMSNorm + three-axis RoPE), optionally fused with the low-bit quantiser.
+struct ProArgs {
+  const void *in;
+  int64_t isb, isn, ish;  // elements
+  void *out;
+  int64_t osb, osn, osh;  // elements (bf16 out) or bytes (int8 codes out)
+  const float *gamma;     // [D]
+  const int32_t *pos;     // [n][3]: t, y, x
+  float eps, base_log2;
+  int32_t n, batch, H;
+  int32_t kind;           // quantised output: 0 = Q, 1 = K (reduced by `mean`)
+  const float *mean;      // [batch][H][D] or NULL
+  float *lse;             // Q with a mean: per-row shift softmax_scale * q.m, [batch][H][n]
+  float softmax_scale;
+  float *scale;           // quantised output: [batch][H][ceil(n/128)]
+};
+
+hipError_t launch_norm_rope(const ProArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_norm_rope_quant(const ProArgs &a, hipStream_t s);
+
 hipError_t launch_w8a8_quant_act(const W8QuantArgs &a, hipStream_t s);
 hipError_t launch_w8a8_quant_weight(const W8QuantArgs &a, hipStream_t s);
 hipError_t launch_w8a8_gemm(const W8GemmArgs &a, hipStream_t s);

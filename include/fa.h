@@ -246,6 +246,39 @@ fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const
                          int32_t frames, fa_hip_stream stream);
 
 /*
+ * QK prologue: RMSNorm over head_dim then rotary position embedding over three
+ * axes, in one pass (the tech report's kernel-fusion paragraph fuses RMSNorm
+ * with elementwise work; the structured summary gives each token stream
+ * condition-specific RoPE positions).  Neither gives formulas; computed:
+ *   y = x / sqrt(mean_d x^2 + eps) * gamma[d]          (gamma [head_dim], all heads)
+ *   the head_dim/2 pairs (d, d + head_dim/2) split into t, y, x groups of
+ *   D/2 - 2*floor(D/6), floor(D/6), floor(D/6) pairs; pair j of a g-pair group
+ *   turns by pos[axis] * rope_base^(-j/g): (a, b) -> (a cos - b sin, a sin + b cos).
+ * pos: int32 [tokens][3] (t, y, x) per token, the caller's choice per stream.
+ * in / out: bf16 [batch][tokens][heads][head_dim] (fa_tensor strides); in may
+ * equal out.  head_dim 64 or 128.  Asynchronous; allocates nothing; argument
+ * errors FA_ERR_INVALID / FA_ERR_UNSUPPORTED before any launch.
+ */
+fa_status fa_qk_norm_rope(const fa_tensor *in, const fa_tensor *out, const float *gamma, float eps,
+                          const int32_t *pos, float rope_base, int32_t tokens, int32_t batch,
+                          int32_t heads, int32_t head_dim, fa_hip_stream stream);
+/*
+ * The same prologue fused with the low-bit quantiser (head_dim 128): writes
+ * int8 codes [batch][tokens][heads][head_dim] (codes->data, byte strides) and
+ * per-(batch, head, 128-token block) scales (codes->scale) exactly as
+ * fa_quantize_lowbit would from the bf16 output of fa_qk_norm_rope: values are
+ * rounded to bf16, keys (is_key = 1) reduced by k_mean [batch][heads][head_dim]
+ * (required), scale absmax/127, codes round half to even.  For queries with
+ * k_mean given, lse_shift [batch][heads][tokens] receives softmax_scale * q.m
+ * (0 = 1/sqrt(head_dim)) -- what fa_attn_fwd adds back to the LSE.
+ */
+fa_status fa_qk_norm_rope_quant(const fa_tensor *in, const fa_tensor *codes, const float *gamma,
+                                float eps, const int32_t *pos, float rope_base, int32_t is_key,
+                                const float *k_mean, float *lse_shift, float softmax_scale,
+                                int32_t tokens, int32_t batch, int32_t heads, int32_t head_dim,
+                                fa_hip_stream stream);
+
+/*
  * Per-block W8A8 linear layer (tech report, paragraph on linear layers: a
  * per-block W8A8 GEMM whose fine-grained scales keep an outlier from setting
  * the range of a whole tensor or channel; the launch article's technical-stack
