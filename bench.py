@@ -475,6 +475,7 @@ def summarize_rocprof(prefix, out_dir):
         copy = max(v for (i, n), v in items if "copyBuffer" in n or "copy" in n.lower())
         factor = (1 << 30) / (copy * 1024.0)
         attn = [v for (i, n), v in items if "attn_bf16" in n]
+        kname = sorted({n for (i, n), v in items if "attn_bf16" in n})
         timed = attn[20:40]  # 20 warm-up launches, then the 20 timed ones
         res[counter] = (factor, sum(timed) / len(timed) * 1024.0 * factor, copy)
     w = W.WORKLOADS[2]
@@ -488,8 +489,9 @@ def summarize_rocprof(prefix, out_dir):
     alg_mean = sum(alg) / len(alg)
     hbm = res["FETCH_SIZE"][1] + res["WRITE_SIZE"][1]
     text = [
-        "# HBM traffic of attn_bf16_kernel<128>, per launch, mean over the 20 timed chunks of the",
-        "# 1560-token 40-head stream (chunks 0..19: warm-up and steady state)",
+        "# HBM traffic of the bf16 attention kernel (%s), per launch," % ", ".join(kname),
+        "# mean over the 20 timed chunks of the 1560-token 40-head stream (chunks 0..19: warm-up",
+        "# and steady state)",
         "# commands (one rocprofv3 pass per counter):",
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s_FETCH_SIZE -o pmc -- %s" % (prefix, cmd),
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s_WRITE_SIZE -o pmc -- %s" % (prefix, cmd),

@@ -31,7 +31,7 @@ class fa_layout_desc(C.Structure):
                 ("chunk_start", C.c_int32), ("window", C.c_int32), ("cache_frames", C.c_int32),
                 ("query_rows", C.c_int32), ("batch", C.c_int32), ("heads", C.c_int32),
                 ("head_dim", C.c_int32), ("dtype", C.c_int32), ("scale", C.c_float),
-                ("sink_frames", C.c_int32)]
+                ("sink_frames", C.c_int32), ("block_rows", C.c_int32)]
 
 
 class fa_tensor(C.Structure):
@@ -144,7 +144,8 @@ def _stream_handle(stream):
 def make_desc(frames: int, tokens_per_frame: int, heads: int, head_dim: int, *, batch: int = 1,
               ref_tokens: Sequence[int] = (), ref_t0: Sequence[int] = (), chunk_start: int = 0,
               window: int = 0, cache_frames: int = 0, query_rows: int = FA_Q_TARGET,
-              dtype: int = FA_BF16, scale: float = 0.0, sink_frames: int = 0) -> fa_layout_desc:
+              dtype: int = FA_BF16, scale: float = 0.0, sink_frames: int = 0,
+              block_rows: int = 0) -> fa_layout_desc:
     d = fa_layout_desc()
     d.frames, d.tokens_per_frame = frames, tokens_per_frame
     d.n_ref = len(ref_tokens)
@@ -154,6 +155,7 @@ def make_desc(frames: int, tokens_per_frame: int, heads: int, head_dim: int, *, 
     d.query_rows, d.batch, d.heads, d.head_dim = query_rows, batch, heads, head_dim
     d.dtype, d.scale = dtype, scale
     d.sink_frames = sink_frames
+    d.block_rows = block_rows
     return d
 
 

@@ -123,7 +123,7 @@ static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t strea
   if (d.dtype == FA_F32)
     e = launch_attn_f32(a, d.head_dim, grid, stream);
   else if (d.dtype == FA_BF16)
-    e = launch_attn_bf16(a, d.head_dim, grid, stream);
+    e = launch_attn_bf16(a, d.head_dim, L->block_m, grid, stream);
   else
     e = launch_attn_lowbit(a, d.head_dim, grid, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));

@@ -1,13 +1,22 @@
 // fa_attn_bf16.hip -- frame-aligned attention forward, bf16 in/out, gfx950.
 //
 // The visibility rule ("Vidu S2" tech report, frame-aligned attention and
-// causal streaming paragraphs) arrives as a block map: per tile of 128 query
-// rows a short list of key ranges (ring runs, chunk, source frames of the
-// tile, visible reference images), each with the mask it needs.  The kernel
-// walks those ranges in 64-key tiles; keys outside them are never loaded.
+// causal streaming paragraphs) arrives as a block map: per work item of 128
+// or 256 query rows a short list of key ranges (ring runs, chunk, source
+// frames of the rows, visible reference images), each with the mask it
+// needs.  The kernels walk those ranges in 64-key tiles; keys outside them
+// are never loaded.
 //
-// Work split.  One workgroup = 4 waves = one query tile of one (batch, head).
-// Each wave owns 32 query rows and computes, per key tile,
+// Two kernels share the arithmetic and the LDS layout:
+//  * attn_bf16_kernel: 4 waves, 128 rows, two workgroups per CU, each wave
+//    interleaving its softmax with its MFMAs;
+//  * attn_bf16_pp_kernel: 8 waves, 256 rows, one workgroup per CU, the two
+//    waves of each SIMD alternating a matrix phase and a softmax phase
+//    ("ping-pong", below).  Each K/V tile then serves twice the rows.
+// The block map picks the work-item height (the ping-pong kernel unless its
+// workgroups need more rounds over the chip than the 128-row ones).
+//
+// Per wave and key tile: 32 query rows,
 //   S^T (64 keys x 32 queries) = K_tile . Q^T   with v_mfma_f32_32x32x16_bf16,
 // so every lane holds one query column and 32 of its scores: the row max and
 // row sum are in-lane, plus one v_permlane32_swap between the lane halves.
@@ -24,9 +33,9 @@
 // LDS and is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16),
 // which hands each lane the 4 keys of one channel its A operand needs.
 //
-// Pipeline.  K tile j+2 and V tile j+1 load while the waves compute
-// softmax(S_j), S_{j+1} = K_{j+1} Q^T and O += V_j P_j; one barrier per
-// tile.  The MFMAs of S_{j+1} do not depend on the softmax of tile j, so
+// Pipeline (4-wave kernel).  K tile j+2 and V tile j+1 load while the waves
+// compute softmax(S_j), S_{j+1} = K_{j+1} Q^T and O += V_j P_j; one barrier
+// per tile.  The MFMAs of S_{j+1} do not depend on the softmax of tile j, so
 // the instruction stream interleaves them (matrix core and VALU overlap).
 //
 // Softmax.  Base-2 online softmax with scale*log2(e) folded into one FMA
@@ -34,6 +43,8 @@
 // exceeds it by more than 8 (so p <= 2^8): the O/l rescale is then rare.
 // Row sums are taken on the bf16-rounded p that feed the PV product
 // (v_dot2c_f32_bf16 against ones).
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -412,11 +423,435 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
         l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
 }
 
-hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int grid, hipStream_t s) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+// Ping-pong kernel.  Waves 0-3 (group A) and 4-7 (group B) share the four
+// SIMDs, one of each per SIMD (waves are dealt to SIMDs round robin).  Time
+// is cut into slots by workgroup barriers: in every slot one group runs its
+// matrix phase (S of the next tile and O += V P of this one: MFMAs and LDS
+// reads only) while the other runs its softmax phase (VALU only), and the
+// roles swap at the barrier, so each SIMD's matrix core is fed by one wave
+// while the other wave's exp work issues beside it.  Group A also issues the
+// direct loads of the pair's K and V tiles, one every few MFMAs of its matrix
+// phase; they have the pair's second slot to land.
+template <int D>
+__global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) {
+  using Cfg = Bf16Cfg<D>;
+  constexpr int BN = Cfg::BN, ROWB = Cfg::ROWB, TILEB = Cfg::TILEB;
+  constexpr float kThr = 8.0f;
+  // LDS: two K and two V tile buffers.  Separate arrays (not one array indexed by buffer) let
+  // the compiler see that direct loads into one buffer never alias reads of another, so it
+  // does not wait for in-flight prefetches before every LDS read.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILEB];
+
+  const DevWork w = cload<DevWork>((const cWork *)a.work + blockIdx.x);
+  if (w.tile < 0) return;
+  const DevTile tile = cload<DevTile>((const cTile *)a.tiles + w.tile);
+  const int b = w.bh / a.H, h = w.bh - (w.bh / a.H) * a.H;
+  const int tid = threadIdx.x;
+  // the wave index is uniform per wave; say so, since it feeds M0 (LDS address of direct loads)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_a = wave < 4;  // group A: matrix phase first in every slot pair
+  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int T = a.T;
+  // a wave whose 32 rows all lie past the tile's end only loads and keeps step
+  const bool wlive = wave * 32 < tile.rows;
+
+  // ---- Q (B operand of S^T): lane holds query row l32 of its wave, channels ds*16 + 8*hl + 0..7
+  const int qloc = wave * 32 + l32;
+  const bool qvalid = qloc < tile.rows;
+  const int qrow = tile.row0 + qloc;
+  bf16x8_t qreg[Cfg::DS];
+  {
+    const Seg qs = a.q[tile.q_kind];
+    const __bf16 *qp = (const __bf16 *)qs.p + b * qs.sb + (int64_t)qrow * qs.sn + h * qs.sh;
+#pragma unroll
+    for (int ds = 0; ds < Cfg::DS; ++ds)
+      qreg[ds] = qvalid ? *(const bf16x8_t *)(qp + ds * 16 + 8 * hl) : bf16x8_t{};
+  }
+  const int fq = qrow / T;  // row frame relative to the chunk (target and source rows)
+
+  // ---- per-lane constants of the LDS reads
+  // K (A operand of S^T): row kb*32 + l32, logical chunk 2*ds + hl.
+  int koff[Cfg::DS];
+#pragma unroll
+  for (int ds = 0; ds < Cfg::DS; ++ds)
+    koff[ds] = l32 * ROWB + (((2 * ds + hl) ^ Cfg::ksw(l32)) * 16);
+  // V (A operand of O^T via the transposing read): lane i = 4s + av of 16-lane group g reads
+  // row ks*16 + r*8 + 4*(g/2) + s, channels db*32 + (g%2)*16 + 4*av .. +3.
+  int voff[Cfg::DB];
+  {
+    const int i = lane & 15, g = lane >> 4;
+    const int s = i >> 2, av = i & 3, hv = g >> 1, gh = g & 1;
+    const int vrow = 4 * hv + s;
+#pragma unroll
+    for (int db = 0; db < Cfg::DB; ++db) {
+      const int lc = db * 4 + gh * 2 + (av >> 1);
+      voff[db] = vrow * ROWB + ((lc ^ Cfg::vsw(vrow)) * 16) + (av & 1) * 8;
+    }
+  }
+  // direct-load row and column of this lane's first load (K and V layouts differ)
+  int krow0, kcb0, vrow0, vcb0;
+  load_map<D, false>(wave, lane, krow0, kcb0);
+  load_map<D, true>(wave, lane, vrow0, vcb0);
+
+  // ---- tile cursors over the flattened (range, 64-key tile) sequence.  Each cursor keeps the
+  // fields of its current range (and, for the load cursors, the (batch, head) base of the
+  // range's tensor) in scalar registers; the block map is only read again when a cursor
+  // crosses into the next range, a few times per work item.
+  const cRange *rng = (const cRange *)a.ranges + tile.r_begin;
+  const int nr = tile.r_count;
+  struct Cur {
+    int r, k, begin, end, mask, param;
+    uint64_t base;  // byte address of (b, key 0, h) of the range's K or V tensor
+    uint32_t sn2;   // bytes between consecutive keys
+  };
+  // kind: 0 = no tensor (mask cursor), 1 = K, 2 = V
+  auto enter = [&](Cur &c, int r, int kind) {
+    while (r < nr && rng[r].begin >= rng[r].end) ++r;
+    c.r = r;
+    if (r >= nr) return;
+    const DevRange R = cload<DevRange>(rng + r);
+    c.k = c.begin = R.begin;
+    c.end = R.end;
+    c.mask = R.mask;
+    c.param = R.param;
+    if (kind) {
+      const Seg sg = kind == 2 ? a.v[R.seg] : a.k[R.seg];
+      c.base = (uint64_t)sg.p + (uint64_t)((int64_t)b * sg.sb + (int64_t)h * sg.sh) * 2u;
+      c.sn2 = (uint32_t)sg.sn * 2u;
+    }
+  };
+  auto next = [&](Cur &c, int kind) {
+    if (c.r >= nr) return;
+    c.k += BN;
+    if (c.k >= c.end) enter(c, c.r + 1, kind);
+  };
+
+  // Buffer descriptor of the tile at cursor c (K or V).  It covers only the keys of the range,
+  // so the hardware returns zeros past its end; a cursor past the last range gets an empty
+  // descriptor (its loads return zeros into a buffer nobody reads again).
+  auto tile_rsrc = [&](const Cur &c) {
+    const bool live = c.r < nr;
+    const uint64_t ub = c.base + (uint64_t)(uint32_t)c.k * c.sn2;
+    const int nvalid = live ? min(BN, c.end - c.k) : 0;
+    return make_rsrc(ub, (int)(nvalid * c.sn2));
+  };
+  auto lane_off = [&](const Cur &c, bool is_v) {
+    return (uint32_t)(is_v ? vrow0 : krow0) * c.sn2 + (uint32_t)(is_v ? vcb0 : kcb0);
+  };
+  // Direct load j of this lane's share of a tile into LDS buffer `buf` (group A waves only).
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off0, uint32_t sn2, char *buf, int j) {
+    const uint32_t off = off0 + (uint32_t)(j * Cfg::RSTEP) * sn2;
+    lds_char *dst = (lds_char *)buf + (4 * j + wave) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
+                                             (int)off, 0, 0, 0);
+  };
+  auto issue = [&](const Cur &c, bool is_v, char *buf) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c);
+    const uint32_t o = lane_off(c, is_v);
+#pragma unroll
+    for (int j = 0; j < Cfg::LOADS; ++j) load_one(rs, o, c.sn2, buf, j);
+  };
+
+  f32x16_t oacc[Cfg::DB];
+#pragma unroll
+  for (int i = 0; i < Cfg::DB; ++i) oacc[i] = f32x16_t{};
+  float m_run = -__builtin_inff();
+  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in four chains
+  const float c = a.c;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};  // S^T of the tile awaiting its softmax
+  u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = u32x4_t{};
+
+  // S^T = K . Q^T, one k-step, both 32-key halves of the tile
+  auto qk_step = [&](const lds_char *Kl, int ds) {
+    const bf16x8_t a0 = *(const bf16x8_t *)(Kl + koff[ds]);
+    const bf16x8_t a1 = *(const bf16x8_t *)(Kl + 32 * ROWB + koff[ds]);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ds], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ds], s1, 0, 0, 0);
+  };
+  // O^T += V^T . P^T, one 16-key slice and one 32-channel block
+  auto pv_step = [&](const lds_char *Vl, int ks, int db) {
+    const lds_char *src = Vl + ks * 16 * ROWB + voff[db];
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(src));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(src + 8 * ROWB));
+    const s16x4_t both[2] = {lo, hi};
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        av, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[db], 0, 0, 0);
+  };
+
+  // Matrix phase: S of the next tile (K in `kbuf`) and O += V P of this one (V in `vbuf`, P in
+  // pw).  After the last tile the S product runs on whatever `kbuf` holds and is dropped: one
+  // straight-line block, so the accumulators keep their registers.  Operand reads run a few
+  // MFMAs ahead.  In group A the phase also issues the pair's direct loads (K at cursor ck
+  // into `kw`, V at cursor cv into `vw`), one every few MFMAs, so they trickle into the
+  // load path instead of queueing behind each other.
+  auto matrix_phase = [&](const char *kbuf, const char *vbuf, auto with_loads, const Cur &kc,
+                          char *kw, const Cur &vc, char *vw) {
+    const lds_char *Kl = (const lds_char *)kbuf, *Vl = (const lds_char *)vbuf;
+    constexpr int NQK = 2 * Cfg::DS, NPV = 4 * Cfg::DB, NL = 2 * Cfg::LOADS;
+    constexpr int EVERY = (NQK + NPV) / NL;
+    s0 = f32x16_t{};
+    s1 = f32x16_t{};
+    if constexpr (decltype(with_loads)::value) {
+      const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
+      const uint32_t kof = lane_off(kc, false), vof = lane_off(vc, true);
+#pragma unroll
+      for (int j = 0; j < Cfg::LOADS; ++j) load_one(krs, kof, kc.sn2, kw, j);
+#pragma unroll
+      for (int j = 0; j < Cfg::LOADS; ++j) load_one(vrs, vof, vc.sn2, vw, j);
+    }
+#pragma unroll
+    for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(Kl, ds);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < Cfg::DB; ++db) pv_step(Vl, ks, db);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read: K operands of k-steps 0, 1
+#pragma unroll
+    for (int i = 0; i < NQK + NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK, then PV)
+      if constexpr (decltype(with_loads)::value)
+        if (i % EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      // operands four MFMAs ahead: K reads (one per QK MFMA), then V reads (two per PV MFMA)
+      if (i + 4 < NQK)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else if (i + 4 < NQK + NPV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
+  // Softmax phase of the tile at mask cursor cc, whose scores are in (s0, s1): mask, row max,
+  // (rare) O rescale, P = exp2(c s - m) into pw, row sum.  Advances cc to the next tile.
+  auto softmax_phase = [&](Cur &cc) {
+    {
+      // mask: s{kb}[i] is key cc.k + kb*32 + (i/4)*8 + 4*hl + i%4 of this lane's query; only
+      // partial tiles and masked ranges come here
+      if (cc.mask != FA_MASK_NONE || cc.k + BN > cc.end) {
+        int klo = cc.begin, khi = cc.end;
+        if (cc.mask == FA_MASK_SAME_FRAME) {
+          klo = max(klo, fq * T);
+          khi = min(khi, (fq + 1) * T);
+        } else if (cc.mask == FA_MASK_GATE && fq < cc.param) {
+          khi = klo;
+        }
+        const int base = cc.k + 4 * hl;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k0i = base + (i >> 2) * 8 + (i & 3);
+          const int k1i = k0i + 32;
+          if (k0i < klo || k0i >= khi) s0[i] = -__builtin_inff();
+          if (k1i < klo || k1i >= khi) s1[i] = -__builtin_inff();
+        }
+      }
+      // row max: in-lane over the 32 scores as a tree of three-way maxima (depth 4), then
+      // across the lane halves
+      float m1[11];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        m1[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+        m1[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
+      }
+      m1[10] = fmaxf(s0[15], s1[15]);
+      const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+      const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
+      float mx = fmaxf(fmaxf(fmaxf(m2a, m2b), m2c), m2d);
+      mx = xhalf_max(mx);
+      // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
+      const float mt = mx * c;
+      const bool need = mt > m_run + kThr;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+      m_run = need ? mt : m_run;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
+      }
+      const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
+                             (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i + 1], c, mneg))};
+        const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg)),
+                             (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i + 1], c, mneg))};
+        l_part[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(e0, ones, l_part[(i >> 1) & 1], false);
+        l_part[2 + ((i >> 1) & 1)] =
+            __builtin_amdgcn_fdot2_f32_bf16(e1, ones, l_part[2 + ((i >> 1) & 1)], false);
+        pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e0);
+        pw[2 + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e1);
+      }
+    }
+    next(cc, 0);
+  };
+
+  // Slot ends.  The first barrier of a slot pair only hands the phases over (no data is
+  // published: the buffers read on both sides of it were filled before the pair began), so it
+  // waits for nothing.  The second one publishes the pair's direct loads: every wave waits for
+  // its own, then the barrier (its fence also completes every LDS read of the pair, freeing
+  // those buffers for the next pair's loads).
+  // A phase's results are pinned before the barrier that ends it: the instruction selector
+  // orders only side-effecting nodes, so without the pins it may place pure arithmetic of one
+  // phase after the barrier, in the next.
+  auto pin_softmax = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __asm__ volatile("" : "+v"(pw[i]));
+    __asm__ volatile("" : "+v"(l_part[0]), "+v"(l_part[1]), "+v"(l_part[2]), "+v"(l_part[3]),
+                     "+v"(m_run));
+  };
+  auto pin_matrix = [&]() {
+    __asm__ volatile("" : "+v"(s0), "+v"(s1));
+#pragma unroll
+    for (int i = 0; i < Cfg::DB; ++i) __asm__ volatile("" : "+v"(oacc[i]));
+  };
+  // Neither barrier may have arithmetic moved across it (the machine scheduler would otherwise
+  // pull the exp work of a softmax phase into the neighbouring matrix phase).
+  auto handover = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto publish = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Cur cc, cv, ck;  // mask cursor (tile awaiting softmax); V loads; K loads
+  enter(cc, 0, 0);
+  if (cc.r < nr) {
+    enter(cv, cc.r, 2);
+    Cur k0c, k1c;  // prologue K tiles 0 and 1
+    enter(k0c, cc.r, 1);
+    k1c = k0c;
+    next(k1c, 1);
+    // prologue: K_0 -> kbuf0, V_0 -> vbuf0, K_1 -> kbuf1; S_0 everywhere, softmax of S_0 in
+    // group A (group B takes it in the first slot)
+    if (grp_a) {
+      issue(k0c, false, kbuf0);
+      issue(cv, true, vbuf0);
+      issue(k1c, false, kbuf1);
+    }
+    next(cv, 2);  // now tile 1
+    ck = k1c;
+    next(ck, 1);  // now tile 2
+    publish();
+    auto advance = [&]() {
+      const bool more = cv.r < nr;  // tile j+1 exists (every wave agrees)
+      next(ck, 1);
+      next(cv, 2);
+      return more;
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    // Slot pair j: loads of K_{j+2} and V_{j+1} (by group A, during its matrix phase); the
+    // matrix phase reads K_{j+1} and V_j.  Even pairs read kbuf1 / vbuf0 and load into kbuf0 /
+    // vbuf1, odd pairs the other way round; unrolled by two so the buffers are compile-time
+    // names.  Group A, group B and the waves without rows run separate copies of the loop
+    // (same barriers), so no copy carries another's register assignment.
+    if (!wlive) {
+      __syncthreads();
+      auto pair = [&](char *kw, char *vw) {
+        if (grp_a) {
+          issue(ck, false, kw);
+          issue(cv, true, vw);
+        }
+        const bool more = advance();
+        handover();
+        publish();
+        return more;
+      };
+      while (pair(kbuf0, vbuf1) && pair(kbuf1, vbuf0)) {
+      }
+    } else {
+      {
+        const lds_char *K0 = (const lds_char *)kbuf0;
+#pragma unroll
+        for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(K0, ds);
+      }
+      if (grp_a) {
+        softmax_phase(cc);
+        __syncthreads();  // every wave has read kbuf0 before the first pair loads K_2 into it
+        auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
+          matrix_phase(kr, vr, yes{}, ck, kw, cv, vw);
+          pin_matrix();
+          const bool more = advance();
+          handover();
+          if (more) {
+            softmax_phase(cc);
+            pin_softmax();
+          }
+          publish();
+          return more;
+        };
+        while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+        }
+      } else {
+        __syncthreads();
+        auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
+          const bool more = advance();
+          softmax_phase(cc);
+          pin_softmax();
+          handover();
+          matrix_phase(kr, vr, no{}, ck, kw, cv, vw);
+          pin_matrix();
+          publish();
+          return more;
+        };
+        while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+  if (!qvalid) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const Seg os = a.o[tile.q_kind];
+  __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh;
+#pragma unroll
+  for (int db = 0; db < Cfg::DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t v;
+      v[0] = (__bf16)(oacc[db][g * 4 + 0] * inv);
+      v[1] = (__bf16)(oacc[db][g * 4 + 1] * inv);
+      v[2] = (__bf16)(oacc[db][g * 4 + 2] * inv);
+      v[3] = (__bf16)(oacc[db][g * 4 + 3] * inv);
+      *(bf16x4_t *)(op + db * 32 + g * 8 + 4 * hl) = v;
+    }
+  }
+  float *lse = a.lse[tile.q_kind];
+  if (lse && hl == 0)
+    lse[(int64_t)w.bh * a.q_rows[tile.q_kind] + qrow] =
+        l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int block_m, int grid,
+                            hipStream_t s) {
+  if (block_m == kBf16PPBlockM) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_pp_kernel<128>, dim3(grid), dim3(512), 0, s, a);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ namespace fa {
 // Tile sizes of the kernels.  The block map is built for the kernel that
 // will consume it: BM query rows per tile, key tiles of BN keys.
 constexpr int kBf16BlockM = 128;   // 4 waves x 32 query rows
+constexpr int kBf16PPBlockM = 256; // ping-pong kernel: 8 waves x 32 query rows
 constexpr int kBf16BlockN = 64;
 constexpr int kF32BlockM = 64;     // one wave, one row per lane
 constexpr int kF32BlockN = 64;
@@ -89,7 +90,8 @@ __host__ __device__ inline int ring_slot(int g, int sink, int cache_frames) {
 }
 
 // Launchers (defined in the .hip files); return hipError_t of the launch.
-hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int block_m, int grid,
+                            hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_attn_lowbit(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);

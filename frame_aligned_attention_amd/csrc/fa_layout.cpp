@@ -34,6 +34,9 @@ static fa_status validate(const fa_layout_desc *d, int32_t ring_first, int32_t *
   if (d->window < FA_WINDOW_ALL) return fail(FA_ERR_INVALID, "window must be >= -1");
   if (d->cache_frames < 0) return fail(FA_ERR_INVALID, "cache_frames must be >= 0");
   if (d->sink_frames < 0) return fail(FA_ERR_INVALID, "sink_frames must be >= 0");
+  if (d->block_rows != 0 && (d->dtype != FA_BF16 || (d->block_rows != kBf16BlockM &&
+                                                      d->block_rows != kBf16PPBlockM)))
+    return fail(FA_ERR_INVALID, "block_rows must be 0, or 128 or 256 with FA_BF16");
   if (d->query_rows <= 0 || d->query_rows > 7)
     return fail(FA_ERR_INVALID, "query_rows must be a non-empty set of FA_Q_* bits");
   if (d->batch < 1 || d->heads < 1) return fail(FA_ERR_INVALID, "batch and heads must be >= 1");
@@ -104,6 +107,27 @@ static void add_ref_ranges(const fa_layout_desc *d, int fa_rel, int fb_rel,
   }
 }
 
+// Query rows per bf16 work item when the caller leaves it open.  The 256-row kernel runs one
+// workgroup per CU, the 128-row kernel two: take 256 unless its workgroups need more rounds
+// over the chip's 256 CUs than the 128-row ones do (a nearly empty last round costs more than
+// the ping-pong kernel gains).
+static int32_t bf16_block_rows(const fa_layout_desc &d) {
+  constexpr int64_t kCUs = 256;
+  auto items = [&](int64_t bm) {
+    const int64_t F = d.frames, T = d.tokens_per_frame;
+    int64_t ref = 0;
+    for (int r = 0; r < d.n_ref; ++r) ref += d.ref_tokens[r];
+    int64_t n = 0;
+    if (d.query_rows & FA_Q_TARGET) n += (F * T + bm - 1) / bm;
+    if (d.query_rows & FA_Q_SOURCE) n += (F * T + bm - 1) / bm;
+    if (d.query_rows & FA_Q_REF) n += (ref + bm - 1) / bm;
+    return n * d.batch * d.heads;
+  };
+  const int64_t r256 = (items(kBf16PPBlockM) + kCUs - 1) / kCUs;
+  const int64_t r128 = (items(kBf16BlockM) + 2 * kCUs - 1) / (2 * kCUs);
+  return r256 <= r128 ? kBf16PPBlockM : kBf16BlockM;
+}
+
 static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout *L) {
   int32_t hist_lo = 0, rf = 0;
   fa_status st = validate(din, ring_first, &hist_lo, &rf);
@@ -116,6 +140,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   L->hist_lo = hist_lo;
   const int T = d.tokens_per_frame, F = d.frames, cs = d.chunk_start;
   L->block_m = d.dtype == FA_F32 ? kF32BlockM : d.dtype == FA_BF16 ? kBf16BlockM : kLowbitBlockM;
+  if (d.dtype == FA_BF16) L->block_m = d.block_rows ? d.block_rows : bf16_block_rows(d);
   L->block_n = d.dtype == FA_F32 ? kF32BlockN : d.dtype == FA_BF16 ? kBf16BlockN : kLowbitBlockN;
   int ref_total = 0;
   for (int r = 0; r < d.n_ref; ++r) ref_total += d.ref_tokens[r];

@@ -93,6 +93,10 @@ typedef struct {
   int32_t dtype;            /* fa_dtype */
   float scale;              /* softmax scale; 0 = 1/sqrt(head_dim) */
   int32_t sink_frames;      /* streaming: frames 0 .. sink_frames-1 stay visible; 0 = none */
+  int32_t block_rows;       /* FA_BF16: query rows per work item, 128 or 256 (the 8-wave
+                               ping-pong kernel); 0 = chosen from the grid (256 unless it needs
+                               more rounds of workgroups over the 256 CUs than 128 does).
+                               Other dtypes: 0 only. */
 } fa_layout_desc;
 
 /* A device tensor [batch][tokens][heads][head_dim], head_dim contiguous. */

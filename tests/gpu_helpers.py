@@ -89,6 +89,7 @@ class Call:
     k_ref: Optional[np.ndarray] = None
     v_ref: Optional[np.ndarray] = None
     sink: int = 0  # frames 0 .. sink-1 stay visible (streaming)
+    block_rows: int = 0  # bf16 work-item rows (128 or 256); 0 = the library's choice
 
     @property
     def fa_dtype(self):
@@ -98,7 +99,8 @@ class Call:
         return B.make_desc(self.C, self.T, self.H, self.D, ref_tokens=self.ref_tokens,
                            ref_t0=self.ref_t0, chunk_start=self.cs, window=self.window,
                            cache_frames=self.cache, query_rows=self.query_rows,
-                           dtype=self.fa_dtype, sink_frames=self.sink)
+                           dtype=self.fa_dtype, sink_frames=self.sink,
+                           block_rows=self.block_rows)
 
     def problem(self) -> O.Problem:
         z = np.zeros((0, self.H, self.D), np.float32)
@@ -115,7 +117,7 @@ class Call:
 
 
 def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tokens=(),
-                ref_t0=(), query_rows=7, scale_k=1.0, sink=0) -> Call:
+                ref_t0=(), query_rows=7, scale_k=1.0, sink=0, block_rows=0) -> Call:
     """Seeded N(0,1) inputs (bf16-rounded unless fp32) for one call."""
     g = np.random.default_rng(seed)
 
@@ -127,7 +129,7 @@ def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tok
     lo = 0 if window < 0 else max(0, cs - window)
     c = Call(T=T, C=C, H=H, D=D, dtype=dtype, cs=cs, window=window, cache=cache,
              ref_tokens=list(ref_tokens), ref_t0=list(ref_t0), query_rows=query_rows,
-             hist_first=(0 if sink else lo) if cache else 0, sink=sink)
+             hist_first=(0 if sink else lo) if cache else 0, sink=sink, block_rows=block_rows)
     c.q = {TGT: n(C * T, H, D), SRC: n(C * T, H, D), REF: n(R, H, D)}
     nh = (cs + C - c.hist_first) * T
     c.k_hist, c.v_hist = n(nh, H, D) * scale_k, n(nh, H, D)

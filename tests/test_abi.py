@@ -86,6 +86,12 @@ def build_status(d, ring_first=-1):
     (dict(sink_frames=5, window=0, cache_frames=4), B.FA_ERR_CAPACITY),  # 5 sink frames, 4 slots
     (dict(sink_frames=6, window=0, cache_frames=6), B.FA_OK),    # history = the 6 sink frames
     (dict(sink_frames=4, window=3, cache_frames=6), B.FA_OK),    # sink reaches the window
+    (dict(block_rows=128), B.FA_OK),
+    (dict(block_rows=256), B.FA_OK),
+    (dict(block_rows=192), B.FA_ERR_INVALID),
+    (dict(block_rows=512), B.FA_ERR_INVALID),
+    (dict(block_rows=128, dtype=B.FA_LOWBIT), B.FA_ERR_INVALID),  # bf16 only
+    (dict(block_rows=128, dtype=B.FA_F32), B.FA_ERR_INVALID),
     (dict(), B.FA_OK),
     (dict(window=0, cache_frames=0), B.FA_OK),
     (dict(chunk_start=0, window=-1, cache_frames=0), B.FA_OK),  # no history at all

@@ -52,11 +52,19 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("br", [128, 256], ids=["bm128", "bm256"])
 @pytest.mark.parametrize("case", SMALL, ids=["s%d" % c[0] for c in SMALL])
-def test_small_shapes(case):
+def test_small_shapes(case, br):
+    """Each bf16 case through both kernels: 128-row work items (4 waves) and 256-row ones
+    (the 8-wave ping-pong kernel)."""
     seed, T, C, H, D, dt, refs, t0s, qr = case
-    G.say("case: small %s" % (case,))
-    c = G.random_call(seed, T, C, H, D, dt, ref_tokens=refs, ref_t0=t0s, query_rows=qr)
+    if dt != "bf16":
+        if br == 256:
+            pytest.skip("block_rows applies to bf16 only")
+        br = 0
+    G.say("case: small %s, block_rows %d" % (case, br))
+    c = G.random_call(seed, T, C, H, D, dt, ref_tokens=refs, ref_t0=t0s, query_rows=qr,
+                      block_rows=br)
     G.compare_all(c, G.run_call(c), "small s%d" % seed)
 
 
@@ -76,12 +84,13 @@ STREAMS = [
 ]
 
 
+@pytest.mark.parametrize("br", [128, 256], ids=["bm128", "bm256"])
 @pytest.mark.parametrize("case", STREAMS, ids=["st%d" % c[0] for c in STREAMS])
-def test_streaming_calls(case):
+def test_streaming_calls(case, br):
     seed, T, C, H, D, cs, win, cap, refs, t0s, *rest = case
-    G.say("case: streaming %s" % (case,))
+    G.say("case: streaming %s, block_rows %d" % (case, br))
     c = G.random_call(seed, T, C, H, D, "bf16", cs=cs, window=win, cache=cap, ref_tokens=refs,
-                      ref_t0=t0s, query_rows=3, sink=rest[0] if rest else 0)
+                      ref_t0=t0s, query_rows=3, sink=rest[0] if rest else 0, block_rows=br)
     G.compare_all(c, G.run_call(c), "stream st%d" % seed)
 
 

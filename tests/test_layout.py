@@ -134,7 +134,7 @@ def test_blockmap_equals_oracle_visibility(case):
 
 
 def test_tile_rows_and_sizes():
-    d = B.make_desc(21, 1560, 12, 128, ref_tokens=[1560], ref_t0=[0], query_rows=7)
+    d = B.make_desc(21, 1560, 12, 128, ref_tokens=[1560], ref_t0=[0], query_rows=7, block_rows=128)
     L = B.fa_layout_build(d)
     n, bm, bn = B.fa_layout_tiles(L)
     assert (bm, bn) == (128, 64)
@@ -147,6 +147,31 @@ def test_tile_rows_and_sizes():
     assert (B.FA_SEG_SRC, 0, 2 * 1560, B.FA_MASK_SAME_FRAME, 0) in ranges
     (kind, row0, rows), ranges = B.fa_layout_tile(L, 11)
     assert (B.FA_SEG_SRC, 0, 1560, B.FA_MASK_NONE, 0) in ranges
+
+
+def test_tile_rows_256():
+    d = B.make_desc(21, 1560, 12, 128, ref_tokens=[1560], ref_t0=[0], query_rows=7, block_rows=256)
+    L = B.fa_layout_build(d)
+    n, bm, bn = B.fa_layout_tiles(L)
+    assert (bm, bn) == (256, 64)
+    assert n == 128 + 128 + 7  # 32760 = 127*256 + 248 rows per kind, 1560 reference rows
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 127)
+    assert (kind, row0, rows) == (0, 127 * 256, 248)
+    # rows 1280..1535 lie in frame 0; rows 1536..1791 straddle frames 0 and 1
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 5)
+    assert (B.FA_SEG_SRC, 0, 1560, B.FA_MASK_NONE, 0) in ranges
+    (kind, row0, rows), ranges = B.fa_layout_tile(L, 6)
+    assert (B.FA_SEG_SRC, 0, 2 * 1560, B.FA_MASK_SAME_FRAME, 0) in ranges
+
+
+@pytest.mark.parametrize("wid,want", [(1, 256), (2, 256), (3, 128)])
+def test_bf16_block_rows_chosen_by_grid(wid, want):
+    """With block_rows 0 a bf16 layout takes 256-row work items (one 8-wave workgroup per CU)
+    unless they need more rounds over 256 CUs than 128-row items two to a CU: the 1560-token
+    bidirectional call (3156 vs 6300 items: 13 rounds each) and stream chunk (760 vs 1480: 3
+    each) take 256, the 3600-token chunk (1032 vs 2040: 5 vs 4 rounds) 128."""
+    _, bm, _ = B.fa_layout_tiles(workload_layout(wid)[2])
+    assert bm == want
 
 
 def workload_layout(wid, cs=None):
