@@ -218,7 +218,13 @@ constexpr int LOADS = TILEB / (256 * 16);       // 2 direct loads per thread per
 __device__ __forceinline__ int sw(int r) { return (r >> 1) & (CH - 1); }
 }  // namespace lb
 
-__global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
+// Work split as in the bf16 kernels: 4 waves of 32 query rows per 128-row work item, keys as the M
+// dimension.  Per 64-key tile: S^T = K Q^T on 8 int8 MFMAs, softmax, O^T += V^T P^T on 4 e4m3
+// MFMAs.  The loads of tile j+1 go out at the start of step j into the other LDS buffers; the
+// step itself runs S, softmax and PV of tile j in order.  With 1-byte tiles (32 KB of LDS per
+// workgroup) and 168 VGPRs, three workgroups share a CU, and the waves of the other two
+// workgroups fill each wave's dependency gaps.
+__global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   using namespace lb;
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
@@ -253,23 +259,15 @@ __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
   const int fq = qrow / T;
 
   // ---- LDS read offsets
-  int koff[4];
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hl) ^ sw(l32)) * 16);
+  const int koff0 = l32 * ROWB + ((hl ^ sw(l32)) * 16);  // k-step ds at koff0 ^ (ds << 5)
   // V^T operand via ds_read_b64_tr_b8: in 16-lane group g, lane i reads 8 bytes of row
   // key(g/2, 8t + i/2), channels db*32 + (g%2)*16 + 8*(i%2) .. +7, for t = 0..3.
-  int voff[4][4];
+  int voff0;  // block db, key slice t at (voff0 ^ (db << 5)) + 16 t rows
   {
     const int i = lane & 15, g = lane >> 4;
     const int hv = g >> 1, gh = g & 1, sp = i >> 1, u = i & 1;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int s = 8 * t + sp, kb = s >> 4, r = s & 15;
-      const int row = kb * 32 + (r >> 2) * 8 + 4 * hv + (r & 3);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        voff[t][db] = row * ROWB + (((2 * db + gh) ^ sw(row)) * 16) + 8 * u;
-    }
+    const int row = (sp >> 2) * 8 + 4 * hv + (sp & 3);
+    voff0 = row * ROWB + ((gh ^ sw(row)) * 16) + 8 * u;
   }
   int lrow[LOADS], lcb[LOADS];
 #pragma unroll
@@ -352,8 +350,8 @@ __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
     s1 = i32x16_t{};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-      const i32x4_t a0 = *(const i32x4_t *)(Kl + koff[ds]);
-      const i32x4_t a1 = *(const i32x4_t *)(Kl + 32 * ROWB + koff[ds]);
+      const i32x4_t a0 = *(const i32x4_t *)(Kl + (koff0 ^ (ds << 5)));
+      const i32x4_t a1 = *(const i32x4_t *)(Kl + 32 * ROWB + (koff0 ^ (ds << 5)));
       s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[ds], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[ds], s1, 0, 0, 0);
     }
@@ -425,7 +423,7 @@ __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2_t *)(Vl + voff[t][db]));
+            (__attribute__((address_space(3))) i32x2_t *)(Vl + (voff0 ^ (db << 5)) + t * 16 * ROWB));
         av[2 * t] = r2[0];
         av[2 * t + 1] = r2[1];
       }
@@ -439,40 +437,36 @@ __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
     __syncthreads();
   };
 
-  Cur cc, ck, cv;  // tile j; K prefetch (j+2); V prefetch (j+1)
+  Cur cc, ck, cv;  // tile j (mask); K and V loads (j+1)
   enter(cc, 0, 0);
   if (cc.r < nr) {
-    Cur k0c, k1c;
-    enter(k0c, cc.r, 1);
-    k1c = k0c;
-    next(k1c, 1);
+    enter(ck, cc.r, 1);
     enter(cv, cc.r, 2);
-    issue(k0c, kbuf0);
+    issue(ck, kbuf0);
     issue(cv, vbuf0);
-    if (k1c.r < nr) issue(k1c, kbuf1);
-    next(cv, 2);
-    ck = k1c;
     next(ck, 1);
+    next(cv, 2);
     end_step();
-    i32x16_t sa0, sa1, sb0, sb1;
-    qk(kbuf0, sa0, sa1);
+    i32x16_t s0, s1;
     while (true) {
-      // even step: S_j in (sa); K of j+1 in kbuf1, V of j in vbuf0
-      if (ck.r < nr) issue(ck, kbuf0);
-      if (cv.r < nr) issue(cv, vbuf1);
-      qk(kbuf1, sb0, sb1);
-      softmax_pv(cc, sa0, sa1, vbuf0);
+      if (ck.r < nr) {
+        issue(ck, kbuf1);
+        issue(cv, vbuf1);
+      }
+      qk(kbuf0, s0, s1);
+      softmax_pv(cc, s0, s1, vbuf0);
       end_step();
-      if (cv.r >= nr) break;
-      next(cc, 0); next(cv, 2); next(ck, 1);
-      // odd step
-      if (ck.r < nr) issue(ck, kbuf1);
-      if (cv.r < nr) issue(cv, vbuf0);
-      qk(kbuf0, sa0, sa1);
-      softmax_pv(cc, sb0, sb1, vbuf1);
+      if (ck.r >= nr) break;
+      next(cc, 0); next(ck, 1); next(cv, 2);
+      if (ck.r < nr) {
+        issue(ck, kbuf0);
+        issue(cv, vbuf0);
+      }
+      qk(kbuf1, s0, s1);
+      softmax_pv(cc, s0, s1, vbuf1);
       end_step();
-      if (cv.r >= nr) break;
-      next(cc, 0); next(cv, 2); next(ck, 1);
+      if (ck.r >= nr) break;
+      next(cc, 0); next(ck, 1); next(cv, 2);
     }
   }
 
