@@ -94,9 +94,11 @@ def test_streaming_calls(case, br):
     G.compare_all(c, G.run_call(c), "stream st%d" % seed)
 
 
-def test_bidirectional_reduced():
-    G.say("case: bidirectional bf16, F=3, T=1560, H=2, all rows, full oracle")
+@pytest.mark.parametrize("br", [128, 256], ids=["bm128", "bm256"])
+def test_bidirectional_reduced(br):
+    G.say("case: bidirectional bf16, F=3, T=1560, H=2, all rows, full oracle, block_rows %d" % br)
     c = workload_call(1, H=2, C=3)
+    c.block_rows = br
     G.compare_all(c, G.run_call(c), "bidir reduced")
 
 
@@ -159,16 +161,23 @@ def stream_call(wid, cs, H=None) -> G.Call:
     return c
 
 
-def test_high_res_chunk_full_size_sampled():
-    G.say("case: 3600-token chunk at cs=12, window 9, two references (t0 = 0, cs+1), H=24")
+@pytest.mark.parametrize("br", [0, 256], ids=["auto", "bm256"])
+def test_high_res_chunk_full_size_sampled(br):
+    """Full size through the kernel the block map picks (128-row items here) and through the
+    ping-pong kernel."""
+    G.say("case: 3600-token chunk at cs=12, window 9, two references (t0 = 0, cs+1), H=24, "
+          "block_rows %d" % br)
     c = stream_call(3, 12)
+    c.block_rows = br
     res = G.run_call(c)
     G.compare_sampled(c, res, n_rows=64, heads=[0, 23], what="hi-res chunk")
 
 
-def test_high_res_chunk_reduced_full_oracle():
-    G.say("case: 3600-token chunk, H=1, every row against the oracle")
+@pytest.mark.parametrize("br", [128, 256], ids=["bm128", "bm256"])
+def test_high_res_chunk_reduced_full_oracle(br):
+    G.say("case: 3600-token chunk, H=1, every row against the oracle, block_rows %d" % br)
     c = stream_call(3, 12, H=1)
+    c.block_rows = br
     G.compare_all(c, G.run_call(c), "hi-res chunk H=1")
 
 
