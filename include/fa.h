@@ -192,6 +192,9 @@ typedef struct {
                        FA_MASK_GATE: rows of frame f >= param see the range, others none */
   int32_t param;    /* FA_MASK_GATE: t0 - chunk_start */
 } fa_range_info;
+/* Tiles of the block map: their count, the query rows per tile (block_m: 64 fp32, 128 low-bit,
+ * 128 or 256 bf16 as the descriptor's block_rows resolved) and the keys per kernel step
+ * (block_n).  Any pointer may be NULL.  FA_ERR_INVALID if L is NULL. */
 fa_status fa_layout_tiles(const fa_layout *L, int32_t *n_tiles, int32_t *block_m, int32_t *block_n);
 /* Copies tile i and up to cap of its ranges. */
 fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile, fa_range_info *ranges,
