@@ -52,7 +52,10 @@ def tol_check(got, want, dtype: str, what: str, lse_got=None, lse_want=None):
     elif dtype == "bf16":
         assert st["max"] <= 1e-2 and st["mean"] <= 1e-3, (what, st)
         if "lse_max" in st:
-            assert st["lse_max"] <= 2e-3, (what, st)
+            # The row sum adds the bf16-rounded p that feed the PV product, so l carries up to
+            # the bf16 unit roundoff 2^-8 relative error when one key dominates a row (rows
+            # with a handful of keys); over many keys the errors average out (~1e-5).
+            assert st["lse_max"] <= 4e-3, (what, st)
     else:
         g = got.ravel()
         w_ = want.ravel()
