@@ -14,7 +14,9 @@
 //  - scores s = (q8 . k8) * sq * sk * softmax_scale, exact running max,
 //    p = 2^(s*log2e - m) in fp32, row sums l of p in fp32;
 //  - P.V in e4m3: p' = p * 448 * sv / U with U the largest V block scale of the
-//    call, so p' <= 448; O = (U / 448) * sum(p' v8) / l.
+//    call, so p' <= 448; O = (U / 448) * sum(p' v8) / l.  The kernel forms p'
+//    directly as 2^(s*log2e - m + log2(448 sv / U)) and adds sum(p') * U / (448 sv)
+//    to l once per tile.
 // Key tiles never straddle a 128-token block (a range's first tile ends at the
 // next 64-key boundary), so K and V scales are uniform per tile.
 #include "fa_device.h"
@@ -213,9 +215,13 @@ constexpr int ROWB = D;                         // bytes per K/V row (1-byte cod
 constexpr int CH = ROWB / 16;                   // 16-byte chunks per row (8)
 constexpr int TILEB = BN * ROWB;                // 8 KB
 constexpr int LOADS = TILEB / (256 * 16);       // 2 direct loads per thread per tile
-// chunk c of row r lives at chunk c ^ ((r >> 1) % 8): 16-lane ds_read_b128 of K (16 rows) and
-// the transposing reads of V (8 rows x two 8-byte halves) land on distinct banks
-__device__ __forceinline__ int sw(int r) { return (r >> 1) & (CH - 1); }
+// Chunk c of row r lives at chunk c ^ sw(r), sw(r) = (bit 2, bit 1, bit 3 of r) as bits 0..2.
+// LDS serves 256 bytes a cycle (64 banks): 16 lanes of a ds_read_b128, 32 lanes of a ds_read_b64.
+// A K read (16 lanes = 16 consecutive rows, one chunk each) needs sw to be one-to-one on the 8
+// rows of each parity, which holds as it is one-to-one on bits 1..3.  A transposing V read (32
+// lanes = rows {a, a+2, a+8, a+10} for two row parities, chunk pairs c, c^1) needs sw >> 1 to be
+// one-to-one on bits 1 and 3, which it is.  Both reads are then free of bank conflicts.
+__device__ __forceinline__ int sw(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
 }  // namespace lb
 
 // Work split as in the bf16 kernels: 4 waves of 32 query rows per 128-row work item, keys as the M
@@ -256,6 +262,7 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   const float sq = *((const cFloat *)qs.scale + (int64_t)w.bh * qs.nblk + tile.row0 / 128);
   const float U = *((const cFloat *)a.v_absmax + w.bh);
   const float cq = sq * a.c;  // times sk gives the log2-domain scale of an int score
+  const float w448u = U > 0.0f ? 448.0f / U : 0.0f;  // times sv gives the V weight of a block
   const int fq = qrow / T;
 
   // ---- LDS read offsets
@@ -283,11 +290,11 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   const int nr = tile.r_count;
   struct Cur {
     int r, k, kend, begin, end, mask, param, seg;
-    uint64_t base;  // byte address of (b, key 0, h) of the range's K or V codes
-    uint32_t sn;    // bytes between consecutive keys
+    uint64_t base, vbase;  // byte addresses of (b, key 0, h) of the range's K and V codes
+    uint32_t sn, vsn;      // bytes between consecutive keys of K and of V
   };
   auto set_end = [&](Cur &c) { c.kend = min(c.end, (c.k & ~(BN - 1)) + BN); };
-  auto enter = [&](Cur &c, int r, int kind) {
+  auto enter = [&](Cur &c, int r) {
     while (r < nr && rng[r].begin >= rng[r].end) ++r;
     c.r = r;
     if (r >= nr) return;
@@ -298,24 +305,26 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
     c.param = R.param;
     c.seg = R.seg;
     set_end(c);
-    if (kind) {
-      const Seg sg = kind == 2 ? a.v[R.seg] : a.k[R.seg];
-      c.base = (uint64_t)sg.p + (uint64_t)((int64_t)b * sg.sb + (int64_t)h * sg.sh);
-      c.sn = (uint32_t)sg.sn;
-    }
+    const Seg ks = a.k[R.seg], vs = a.v[R.seg];
+    c.base = (uint64_t)ks.p + (uint64_t)((int64_t)b * ks.sb + (int64_t)h * ks.sh);
+    c.sn = (uint32_t)ks.sn;
+    c.vbase = (uint64_t)vs.p + (uint64_t)((int64_t)b * vs.sb + (int64_t)h * vs.sh);
+    c.vsn = (uint32_t)vs.sn;
   };
-  auto next = [&](Cur &c, int kind) {
+  auto next = [&](Cur &c) {
     if (c.r >= nr) return;
     c.k = c.kend;
     if (c.k >= c.end)
-      enter(c, c.r + 1, kind);
+      enter(c, c.r + 1);
     else
       set_end(c);
   };
-  auto tile_rsrc = [&](const Cur &c) {
+  // buffer descriptors of the K and V codes of the tile at cursor c; past the last range they
+  // are empty (their loads return zeros into a buffer nobody reads again)
+  auto tile_rsrc = [&](const Cur &c, uint64_t base, uint32_t sn) {
     const bool live = c.r < nr;
-    const uint64_t ub = c.base + (uint64_t)(uint32_t)c.k * c.sn;
-    return make_rsrc(ub, live ? (int)((c.kend - c.k) * c.sn) : 0);
+    const uint64_t ub = base + (uint64_t)(uint32_t)c.k * sn;
+    return make_rsrc(ub, live ? (int)((c.kend - c.k) * sn) : 0);
   };
   auto load_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t sn, char *buf, int j) {
     const uint32_t off = (uint32_t)lrow[j] * sn + lcb[j];
@@ -323,10 +332,12 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
                                              (int)off, 0, 0, 0);
   };
-  auto issue = [&](const Cur &c, char *buf) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c);
+  auto issue = [&](const Cur &c, char *kbuf, char *vbuf) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(c, c.base, c.sn), rv = tile_rsrc(c, c.vbase, c.vsn);
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) load_one(rs, c.sn, buf, j);
+    for (int j = 0; j < LOADS; ++j) load_one(rk, c.sn, kbuf, j);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) load_one(rv, c.vsn, vbuf, j);
   };
   // per-tile scales of the tile at cursor c: log2-domain score factor and the V weight
   auto tile_scales = [&](const Cur &c, float &fk, float &wv) {
@@ -335,7 +346,7 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
     const float sk = *((const cFloat *)ks.scale + (int64_t)w.bh * ks.nblk + blk);
     const float sv = *((const cFloat *)vs.scale + (int64_t)w.bh * vs.nblk + blk);
     fk = fmaxf(cq * sk, 1e-30f);  // an all-zero Q or K block: scores 0, masks stay -inf
-    wv = U > 0.0f ? 448.0f * sv / U : 0.0f;
+    wv = sv * w448u;
   };
 
   f32x16_t oacc[4];
@@ -361,6 +372,11 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   auto softmax_pv = [&](const Cur &c, const i32x16_t &s0, const i32x16_t &s1, const char *vbuf) {
     float fk, wv;
     tile_scales(c, fk, wv);
+    // p' = p * wv is formed as 2^(s fk - m + log2 wv), and the row sum takes sum(p') / wv once
+    // per tile.  A zero weight (an all-zero V block) is raised to 2^-60: p' <= 2^-60 still codes
+    // to 0 in e4m3, and sum(p') * 2^60 still gives the row sum.
+    const float wvc = fmaxf(wv, 0x1p-60f);
+    const float lw = __builtin_amdgcn_logf(wvc), iw = __builtin_amdgcn_rcpf(wvc);
     float x0[16], x1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -399,8 +415,9 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
     }
-    const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
-    i32x8_t pw;  // P^T: byte kb*16 + r of the lane's 32 keys
+    const float mneg = (m_run == -__builtin_inff() ? 0.0f : -m_run) + lw;
+    float lt = 0.0f;  // sum of p' over the tile
+    i32x8_t pw;       // P^T: byte kb*16 + r of the lane's 32 keys
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
       float e[8];
@@ -410,12 +427,16 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
         e[4 + j] = __builtin_amdgcn_exp2f(fmaf(x1[i + j], fk, mneg));
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) l_part += e[j];
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0] * wv, e[1] * wv, 0, false);
-      pw[i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2] * wv, e[3] * wv, v, true);
-      v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4] * wv, e[5] * wv, 0, false);
-      pw[4 + i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[6] * wv, e[7] * wv, v, true);
+      for (int j = 0; j < 8; ++j) lt += e[j];
+      // each packing writes one half of its word and keeps the other: the first of a pair is
+      // seeded with a dead register instead of a zero
+      const int o0 = __builtin_bit_cast(int, e[0]), o1 = __builtin_bit_cast(int, e[4]);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], o0, false);
+      pw[i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4], e[5], o1, false);
+      pw[4 + i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[6], e[7], v, true);
     }
+    l_part = fmaf(lt, iw, l_part);
     const lds_char *Vl = (const lds_char *)vbuf;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -437,36 +458,31 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
     __syncthreads();
   };
 
-  Cur cc, ck, cv;  // tile j (mask); K and V loads (j+1)
-  enter(cc, 0, 0);
-  if (cc.r < nr) {
-    enter(ck, cc.r, 1);
-    enter(cv, cc.r, 2);
-    issue(ck, kbuf0);
-    issue(cv, vbuf0);
-    next(ck, 1);
-    next(cv, 2);
+  // One cursor walks the tiles for the loads (tile j+1 during step j); the tile of the step
+  // itself (mask, scales) is a copy taken before each advance.
+  Cur cc, ck;
+  enter(ck, 0);
+  if (ck.r < nr) {
+    cc = ck;
+    issue(ck, kbuf0, vbuf0);
+    next(ck);
     end_step();
     i32x16_t s0, s1;
     while (true) {
-      if (ck.r < nr) {
-        issue(ck, kbuf1);
-        issue(cv, vbuf1);
-      }
+      if (ck.r < nr) issue(ck, kbuf1, vbuf1);
       qk(kbuf0, s0, s1);
       softmax_pv(cc, s0, s1, vbuf0);
       end_step();
       if (ck.r >= nr) break;
-      next(cc, 0); next(ck, 1); next(cv, 2);
-      if (ck.r < nr) {
-        issue(ck, kbuf0);
-        issue(cv, vbuf0);
-      }
+      cc = ck;
+      next(ck);
+      if (ck.r < nr) issue(ck, kbuf0, vbuf0);
       qk(kbuf1, s0, s1);
       softmax_pv(cc, s0, s1, vbuf1);
       end_step();
       if (ck.r >= nr) break;
-      next(cc, 0); next(ck, 1); next(cv, 2);
+      cc = ck;
+      next(ck);
     }
   }
 
