@@ -6,15 +6,15 @@
 // Quantisers: scale = absmax/127, code = round_half_even(x * (127/absmax)) clamped to +-127,
 // the same arithmetic as the attention path's quantiser.
 //
-// GEMM.  One workgroup (4 waves) per 128 (n) x 128 (m) output tile.  Every 128-column K-block
-// is one quantisation block: the int32 products of its four 32-deep k-steps accumulate in the
-// MFMA (v_mfma_i32_32x32x32_i8, exact), then are dequantised into fp32 accumulators with the
-// block's two scales -- one K-block later, beside the next block's MFMAs.  The product is
-// computed as y^T = w . x^T (weights as the A operand), so
-// each lane's output column is one activation row: the activation scale is one register per
-// 32-row tile and the weight scale is uniform per workgroup.  Operand tiles go straight from
-// HBM into double-buffered LDS (direct loads, bounds-checked descriptors zero-fill rows past
-// m), rows XOR-swizzled in 16-byte chunks for conflict-free MFMA operand reads.
+// GEMM.  One workgroup (8 waves, one per CU) per 256 (m) x 128 (n) output tile.  Every
+// 128-column K-block is one quantisation block: the int32 products of its four 32-deep k-steps
+// accumulate in the MFMA (v_mfma_i32_32x32x32_i8, exact), then are dequantised into fp32
+// accumulators with the block's two scales.  The product is computed as y^T = w . x^T (weights
+// as the A operand), so each lane's output column is one activation row: the activation scale
+// is one register per 32-row tile and the weight scale is uniform per workgroup.  Operand tiles
+// go straight from HBM into a 3-stage LDS ring (direct loads, bounds-checked descriptors
+// zero-fill rows past m), rows XOR-swizzled in 16-byte chunks for conflict-free MFMA operand
+// reads; a K-block's loads have two steps to land.
 #include "fa_device.h"
 
 namespace fa {
@@ -141,21 +141,29 @@ __device__ inline bool w8a8_item(int slot, int mt_count, int nt_count, int &mt, 
 }
 
 namespace w8 {
-constexpr int BM = 128, BN = 128, BK = 128;  // output tile (m, n); K-block = quantisation block
-constexpr int TILEB = 128 * BK;             // bytes of one operand tile (128 rows x 128 int8)
-constexpr int LOADS = TILEB / (256 * 16);   // 16-byte direct loads per thread per operand tile
-constexpr int RSTEP = 256 * 16 / BK;        // rows covered by one load of all lanes (32)
+constexpr int BM = 256, BN = 128, BK = 128;  // output tile (m, n); K-block = quantisation block
+constexpr int NTHR = 512;                   // 8 waves, each a 64 (n) x 64 (m) corner
+constexpr int XTILE = BM * BK;              // bytes of one activation stage (32 KB)
+constexpr int WTILE = BN * BK;              // bytes of one weight stage (16 KB)
+constexpr int XLOADS = XTILE / (NTHR * 16); // 16-byte direct loads per thread per stage (4)
+constexpr int WLOADS = WTILE / (NTHR * 16); // (2)
+constexpr int RSTEP = NTHR * 16 / BK;       // rows covered by one load of all lanes (64)
 // chunk c of row r lives at chunk c ^ ((r >> 1) & 7): a ds_read_b128 of 16 lanes (16 rows at
 // one logical chunk) then touches 16 distinct (row parity, chunk) bank groups
 __device__ __forceinline__ int sw(int r) { return (r >> 1) & 7; }
 }  // namespace w8
 
-__global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
+// 256 (m) x 128 (n) output tile per workgroup, one workgroup per CU, K-blocks through a 3-stage
+// LDS ring (48 KB a stage): block kb+2 is loaded while block kb is multiplied, so a load has two
+// steps to land.
+__global__ void __launch_bounds__(512, 1) w8a8_gemm_kernel(const W8GemmArgs a) {
   using namespace w8;
-  __shared__ __attribute__((aligned(1024))) char xb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char xb1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char wb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char wb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char xs0[XTILE];
+  __shared__ __attribute__((aligned(1024))) char xs1[XTILE];
+  __shared__ __attribute__((aligned(1024))) char xs2[XTILE];
+  __shared__ __attribute__((aligned(1024))) char ws0[WTILE];
+  __shared__ __attribute__((aligned(1024))) char ws1[WTILE];
+  __shared__ __attribute__((aligned(1024))) char ws2[WTILE];
 
   const int mt_count = (a.m + BM - 1) / BM, nt_count = a.n / BN;
   int mt, nt;
@@ -166,9 +174,9 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int wn = wave >> 1, wm = wave & 1;  // wave's 64 x 64 corner: n rows wn*64.., m rows wm*64..
+  const int wn = wave >> 2, wm = wave & 3;  // wave's corner: n rows wn*64.., m rows wm*64..
 
-  // direct loads: load j of wave w fills LDS chunks (4j + w)*64 + lane = row row0 + j*RSTEP,
+  // direct loads: load j of wave w fills LDS chunks (8j + w)*64 + lane = row lrow0 + j*RSTEP,
   // logical chunk lc (the swizzle is the same for every j since RSTEP is a multiple of 16)
   const int p0 = wave * 64 + lane;
   const int lrow0 = p0 / 8;
@@ -180,14 +188,20 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
       make_rsrc((uint64_t)a.xq + (uint64_t)m0 * a.ld_xq, (int)((int64_t)xrows * a.ld_xq));
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc((uint64_t)a.wq + (uint64_t)n0 * a.ld_wq, (int)((int64_t)BN * a.ld_wq));
+  // Loads of K-block kb into one stage.  Steps issue them unconditionally (a fixed count of
+  // vector loads per step keeps the waits exact); past the last block they read columns beyond
+  // k of the same rows, or zeros past the descriptor's end, into a stage nobody multiplies.
   auto issue = [&](int kb, char *xdst, char *wdst) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      lds_char *dx = (lds_char *)xdst + (4 * j + wave) * 1024;
-      lds_char *dw = (lds_char *)wdst + (4 * j + wave) * 1024;
+    for (int j = 0; j < XLOADS; ++j) {
+      lds_char *dx = (lds_char *)xdst + (8 * j + wave) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrs, (__attribute__((address_space(3))) void *)dx, 16,
           (int)(xoff0 + (uint32_t)(j * RSTEP) * (uint32_t)a.ld_xq + kb * BK), 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < WLOADS; ++j) {
+      lds_char *dw = (lds_char *)wdst + (8 * j + wave) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wrs, (__attribute__((address_space(3))) void *)dw, 16,
           (int)(woff0 + (uint32_t)(j * RSTEP) * (uint32_t)a.ld_wq + kb * BK), 0, 0, 0);
@@ -199,7 +213,8 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) coff[ks] = (((2 * ks + hl) ^ sw(l32)) * 16);
 
-  // activation scales: lane's row is m0 + wm*64 + tm*32 + l32; rows past m read 0 (bounds)
+  // activation scales: lane's row is m0 + wm*64 + tm*32 + l32; rows past m and blocks past the
+  // last read 0 (bounds)
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc((uint64_t)a.sx, (int)((int64_t)kbt * a.ld_sx * 4));
   auto load_sx = [&](int kb, float (&s)[2]) {
@@ -248,52 +263,64 @@ __global__ void __launch_bounds__(256, 2) w8a8_gemm_kernel(const W8GemmArgs a) {
         for (int i = 0; i < 16; ++i) acc[tn][tm][i] = fmaf((float)part[tn][tm][i], s, acc[tn][tm][i]);
     }
   };
-  // One pipeline step: the MFMAs of K-block kb (tiles in xbuf / wbuf) into pn while the
-  // products of block kb-1 (pp, scales sx and swk) are dequantised; the two are independent,
-  // so the schedule puts the dequantisation beside the MFMAs.
-  auto step = [&](const char *xbuf, const char *wbuf, i32x16_t (&pn)[2][2],
-                  const i32x16_t (&pp)[2][2], const float (&sx)[2], float swk) {
-    mfmas(xbuf, wbuf, pn);
-    dequant(pp, sx, swk);
+  // Each wave has waited for its own loads of the block to publish; the barrier (no fence: a
+  // fence would wait for every load in flight) then makes them visible, and since a wave's LDS
+  // reads of a stage are consumed by MFMAs issued before it, the stage is free afterwards.
+  auto publish = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Step kb: scales of block kb, then the tiles of block kb+2 (in that order, so that waiting
+  // for the scales leaves the tile loads in flight); then the MFMAs of block kb (stage kb % 3)
+  // and their dequantisation (the other wave on the SIMD covers the wait for the products).  At
+  // the end each wave waits for all but this step's tile loads (block kb+1 has landed) and the
+  // barrier publishes them.  The waits are s_waitcnt builtins, which the compiler's own wait
+  // counting sees (an inline-asm wait is opaque to it, and it then inserts full waits).
+  i32x16_t part[2][2];
+  auto step = [&](int kb, const char *xbuf, const char *wbuf, char *xnext, char *wnext) {
+    float s[2];
+    load_sx(kb, s);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 2, xnext, wnext);
+    const float swk = swp[kb];
+    mfmas(xbuf, wbuf, part);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS: operands of k-step 0
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i % 4 == 0 && i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS
-      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (prefetch)
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU (dequantisation)
     }
-  };
-  auto sync = [&]() {
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    dequant(part, s, swk);
+    static_assert(XLOADS + WLOADS == 6, "wait count below");
+    __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6), a wait the compiler's counter sees
+    publish();
   };
 
-  // K-block kb's tiles sit in buffers kb % 2; its products are dequantised one step later.  A
-  // last drain step (kb == kbt) dequantises the final block; its MFMAs read whatever the buffer
-  // holds and their products are dropped (int8 products cannot be NaN).
-  float sxa[2], sxb[2];
-  i32x16_t pa[2][2], pb[2][2];
-  issue(0, xb0, wb0);
-  load_sx(0, sxa);
-  sync();
-  if (kbt > 1) issue(1, xb1, wb1);
-  mfmas(xb0, wb0, pa);
-  sync();
-  for (int kb = 1;;) {
-    // odd kb: tiles in buffers 1, products into pb; block kb-1 in pa / sxa
-    if (kb + 1 < kbt) issue(kb + 1, xb0, wb0);
-    if (kb < kbt) load_sx(kb, sxb);
-    step(xb1, wb1, pb, pa, sxa, swp[kb - 1]);
-    sync();
-    if (++kb > kbt) break;
-    // even kb: tiles in buffers 0, products into pa; block kb-1 in pb / sxb
-    if (kb + 1 < kbt) issue(kb + 1, xb1, wb1);
-    if (kb < kbt) load_sx(kb, sxa);
-    step(xb0, wb0, pa, pb, sxb, swp[kb - 1]);
-    sync();
-    if (++kb > kbt) break;
+  issue(0, xs0, ws0);
+  issue(1, xs1, ws1);
+  __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6): block 0
+  publish();
+  // Unrolled so every stage is a compile-time name (the compiler then knows which LDS array a
+  // load in flight writes).  At the loop head it still waits for the newest loads, so six steps
+  // per iteration rather than three halve that cost.
+  for (int kb = 0;;) {
+    step(kb, xs0, ws0, xs2, ws2);
+    if (++kb >= kbt) break;
+    step(kb, xs1, ws1, xs0, ws0);
+    if (++kb >= kbt) break;
+    step(kb, xs2, ws2, xs1, ws1);
+    if (++kb >= kbt) break;
+    step(kb, xs0, ws0, xs2, ws2);
+    if (++kb >= kbt) break;
+    step(kb, xs1, ws1, xs0, ws0);
+    if (++kb >= kbt) break;
+    step(kb, xs2, ws2, xs1, ws1);
+    if (++kb >= kbt) break;
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the workgroup
 
   // epilogue: y[m][n] bf16; lane's m = m0 + wm*64 + tm*32 + l32, n = n0 + wn*64 + tn*32 +
   // (i/4)*8 + 4*hl + i%4 (four consecutive columns per group of four accumulator registers)
@@ -329,9 +356,9 @@ hipError_t launch_w8a8_quant_weight(const W8QuantArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_w8a8_gemm(const W8GemmArgs &a, hipStream_t s) {
-  const int grid = w8a8_grid((a.m + 127) / 128, a.n / 128);
+  const int grid = w8a8_grid((a.m + w8::BM - 1) / w8::BM, a.n / w8::BN);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(grid), dim3(w8::NTHR), 0, s, a);
   return hipGetLastError();
 }
 

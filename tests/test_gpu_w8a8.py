@@ -66,6 +66,8 @@ CASES = [  # m, n, k, leading-dimension padding
     (130, 128, 256, 16),   # ragged m across two tiles, padded rows
     (300, 384, 640, 0),
     (257, 128, 1024, 32),
+    (513, 1024, 768, 0),    # 8 n tiles (the XCD-grouped order), 6 K-blocks: one unrolled loop pass
+    (600, 1152, 1664, 16),  # 9 n tiles split unevenly over the XCDs, 13 K-blocks
 ]
 
 
