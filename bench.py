@@ -143,6 +143,21 @@ def run_stream_bench(args, torch, W, B):
     }
 
 
+def settle(torch, fn, ms=150.0, cap=400):
+    """Run fn for about `ms` of GPU time before a timed loop.  Inputs are generated on the host
+    just before each workload, the GPU idles meanwhile, and its clocks ramp back up during the
+    first calls; a few warm-up calls are not enough to cover that."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(cap, int(ms / one) + 1)):
+        fn()
+    torch.cuda.synchronize()
+
+
 def time_single_call(wid, torch, W, B, reps=10, sink=0):
     """One-shot workloads (bidirectional 21x1560, 3600-token chunk, the steady chunk of the
     1560-token stream with sink frames): attention call only."""
@@ -177,8 +192,7 @@ def time_single_call(wid, torch, W, B, reps=10, sink=0):
         t["lse_" + nm] = torch.empty((1, w.H, n), dtype=torch.float32, device="cuda")
     io = B.make_io(t)
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        B.fa_attn_fwd(L, io, stream)
+    settle(torch, lambda: B.fa_attn_fwd(L, io, stream))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     torch.cuda.synchronize()
     for e in ev:
@@ -224,9 +238,8 @@ def time_lowbit_chunk(torch, W, B, reps=10):
                       "v_absmax": out["v_absmax"]}, scales)
     io_a = B.make_io({**codes, **out}, scales)
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        B.fa_quantize_lowbit(L, io_in, io_q, 0, stream)
-        B.fa_attn_fwd(L, io_a, stream)
+    settle(torch, lambda: (B.fa_quantize_lowbit(L, io_in, io_q, 0, stream),
+                           B.fa_attn_fwd(L, io_a, stream)))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
     torch.cuda.synchronize()
     for e in ev:
@@ -297,8 +310,7 @@ def time_graph_chunk(torch, W, B, lowbit, reps=20):
 
     def timed(fn):
         stream = torch.cuda.current_stream()
-        for _ in range(3):
-            fn()
+        settle(torch, fn)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize()
         for e in ev:
@@ -336,8 +348,7 @@ def time_w8a8(torch, W, B, reps=10):
     wt = wd.t().contiguous()  # w^T [k, n] as a plain contiguous operand
 
     def timed(fn):
-        for _ in range(3):
-            fn()
+        settle(torch, fn)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize()
         for e in ev:
@@ -374,8 +385,7 @@ def time_prologue(torch, W, B, reps=10):
     scales = torch.empty((1, H, (n + 127) // 128), dtype=torch.float32, device="cuda")
 
     def timed(fn):
-        for _ in range(3):
-            fn()
+        settle(torch, fn)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize()
         for e in ev:
