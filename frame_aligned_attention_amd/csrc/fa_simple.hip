@@ -11,32 +11,35 @@
 
 namespace fa {
 
+// One thread per 16-byte piece of a (token, head) row: blockIdx.y = 2*batch + tensor (K, V),
+// blockIdx.x a run of 256 / chunks16 rows of that tensor's chunk, rows in (token, head) order, so
+// a workgroup reads and writes contiguous spans.  32-bit index arithmetic (rows per tensor and
+// batch stay far below 2^31); the byte offsets are 64-bit.
 __global__ void __launch_bounds__(256) ring_append_kernel(const RingArgs a) {
-  const int64_t per_b = (int64_t)a.frames * a.T * a.H * a.chunks16;
-  const int64_t total = per_b * a.batch * 2;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = idx;
-    const int c = (int)(r % a.chunks16); r /= a.chunks16;
-    const int h = (int)(r % a.H); r /= a.H;
-    const int tok = (int)(r % ((int64_t)a.frames * a.T)); r /= (int64_t)a.frames * a.T;
-    const int b = (int)(r % a.batch); r /= a.batch;
-    const int i = (int)r;  // 0: K, 1: V
-    const int fi = tok / a.T, t = tok - fi * a.T;
-    const int slot = ring_slot(a.first_frame + fi, a.sink, a.cache_frames);
-    const char *src = (const char *)a.src[i] + b * a.ssb[i] + tok * a.ssn[i] + h * a.ssh[i] + c * 16;
-    char *dst = (char *)a.dst[i] + b * a.dsb[i] + ((int64_t)slot * a.T + t) * a.dsn[i] +
-                h * a.dsh[i] + c * 16;
-    *(uint4 *)dst = *(const uint4 *)src;
-  }
+  const int lg = __builtin_ctz(a.chunks16);  // chunks16 is 8, 16 or 32
+  const int rows = a.frames * a.T * a.H;
+  const int row = (int)blockIdx.x * (256 >> lg) + ((int)threadIdx.x >> lg);
+  if (row >= rows) return;
+  const int c = (int)threadIdx.x & (a.chunks16 - 1);
+  const int i = (int)blockIdx.y & 1, b = (int)blockIdx.y >> 1;  // i 0: K, 1: V
+  const int tok = row / a.H, h = row - tok * a.H;
+  const int fi = tok / a.T, t = tok - fi * a.T;
+  const int slot = ring_slot(a.first_frame + fi, a.sink, a.cache_frames);
+  const char *src = (const char *)a.src[i] + b * a.ssb[i] + tok * a.ssn[i] + h * a.ssh[i] + c * 16;
+  char *dst = (char *)a.dst[i] + b * a.dsb[i] + ((int64_t)slot * a.T + t) * a.dsn[i] +
+              h * a.dsh[i] + c * 16;
+  *(uint4 *)dst = *(const uint4 *)src;
 }
 
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s) {
-  const int64_t total = (int64_t)a.frames * a.T * a.H * a.chunks16 * a.batch * 2;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (a.chunks16 != 8 && a.chunks16 != 16 && a.chunks16 != 32) return hipErrorInvalidValue;
+  const int64_t rows = (int64_t)a.frames * a.T * a.H;
+  if (rows < 1 || a.batch < 1) return hipSuccess;
+  if (rows > INT32_MAX || 2LL * a.batch > 65535) return hipErrorInvalidValue;
+  const int per_block = 256 / a.chunks16;
+  const int64_t blocks = (rows + per_block - 1) / per_block;
+  hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)blocks, (unsigned)(2 * a.batch)), dim3(256),
+                     0, s, a);
   return hipGetLastError();
 }
 
