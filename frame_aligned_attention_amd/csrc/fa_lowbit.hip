@@ -121,20 +121,24 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
   float x[8][8];
   bool live[8];
   float amax = 0.0f;
+  // The eight row loads go out together: a row outside the runs reads row min(tok, n - 1), which
+  // lies inside the tensor, and its values are dropped.  (Loads under a per-row branch were
+  // issued one at a time, each waited for before the next.)
+  const __bf16 *in_bh = (const __bf16 *)g.in + b * g.isb + h * g.ish + c0;
+  bf16x8_t v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int tok = blk * 128 + j * 16 + rsub;
     live[j] = in_runs(g, tok);
-    if (live[j]) {
-      const bf16x8_t v = *(const bf16x8_t *)((const __bf16 *)g.in + b * g.isb +
-                                             (int64_t)tok * g.isn + h * g.ish + c0);
+    v[j] = *(const bf16x8_t *)(in_bh + (int64_t)min(tok, g.n - 1) * g.isn);
+  }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[j][i] = g.kind == 1 ? (float)v[i] - m[i] : (float)v[i];
+  for (int j = 0; j < 8; ++j) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[j][i]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[j][i] = 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const float e = g.kind == 1 ? (float)v[j][i] - m[i] : (float)v[j][i];
+      x[j][i] = live[j] ? e : 0.0f;
+      amax = fmaxf(amax, fabsf(x[j][i]));
     }
   }
   if (g.kind == 0 && g.lse) {
