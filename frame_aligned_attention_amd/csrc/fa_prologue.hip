@@ -53,11 +53,11 @@ __device__ __forceinline__ void lane_angles(const int *pos3, const float (&theta
   }
 }
 
-// RMSNorm + RoPE of one row held as 8 values per lane (LPR lanes per row) with the row's
-// rotation sines and cosines; leaves the result rounded to bf16 (as a tensor written by the
-// unfused kernel would hold it), as floats.
+// RMSNorm + RoPE of one row held as 8 values per lane (LPR lanes per row) with the lane's 8
+// norm weights and the row's rotation sines and cosines; leaves the result rounded to bf16 (as a
+// tensor written by the unfused kernel would hold it), as floats.
 template <int D>
-__device__ __forceinline__ void norm_rope_row(float (&x)[8], int lanec, const float *gamma,
+__device__ __forceinline__ void norm_rope_row(float (&x)[8], int lanec, const float (&gamma)[8],
                                              float eps, const float (&sn)[8],
                                              const float (&cs)[8]) {
   constexpr int LPR = D / 8, HALF = LPR / 2;
@@ -69,7 +69,7 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[8], int lanec, const fl
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
   float y[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = x[k] * r * gamma[lanec * 8 + k];
+  for (int k = 0; k < 8; ++k) y[k] = x[k] * r * gamma[k];
   const bool first = lanec < HALF;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -94,17 +94,23 @@ __global__ void __launch_bounds__(256) norm_rope_kernel(const ProArgs a) {
   int axis[8];
   pro::lane_freqs<D>(lanec, a.base_log2, theta, axis);
   pro::lane_angles(a.pos + 3 * t, theta, axis, sn, cs);
+  float gam[8];  // the lane's norm weights, loaded once for every row
+#pragma unroll
+  for (int k = 0; k < 8; ++k) gam[k] = a.gamma[lanec * 8 + k];
+  const __bf16 *in_t = (const __bf16 *)a.in + b * a.isb + (int64_t)t * a.isn + lanec * 8;
+  __bf16 *out_t = (__bf16 *)a.out + b * a.osb + (int64_t)t * a.osn + lanec * 8;
+  // One pass of RPW heads at a time: with 256-thread workgroups per token the CU holds enough
+  // of them to cover the load latency (batching the passes' loads was slower).
   for (int h = rsub; h < a.H; h += RPW) {  // a row's lanes share h
-    const bf16x8_t v = *(const bf16x8_t *)((const __bf16 *)a.in + b * a.isb +
-                                           (int64_t)t * a.isn + h * a.ish + lanec * 8);
+    const bf16x8_t v = *(const bf16x8_t *)(in_t + h * a.ish);
     float x[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = (float)v[k];
-    pro::norm_rope_row<D>(x, lanec, a.gamma, a.eps, sn, cs);
+    pro::norm_rope_row<D>(x, lanec, gam, a.eps, sn, cs);
     bf16x8_t o;
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[k] = (__bf16)x[k];
-    *(bf16x8_t *)((__bf16 *)a.out + b * a.osb + (int64_t)t * a.osn + h * a.osh + lanec * 8) = o;
+    *(bf16x8_t *)(out_t + h * a.osh) = o;
   }
 }
 
@@ -125,30 +131,36 @@ __global__ void __launch_bounds__(256) norm_rope_quant_kernel(const ProArgs a) {
   float m[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) m[k] = a.mean ? a.mean[(int64_t)bh * D + lanec * 8 + k] : 0.0f;
+  float gam[8];  // the lane's norm weights, loaded once for every row
+#pragma unroll
+  for (int k = 0; k < 8; ++k) gam[k] = a.gamma[lanec * 8 + k];
   float x[8][8];
   bool live[8];
   float amax = 0.0f;
+  // The eight row loads go out together: a row past the last token reads the last token's row
+  // (and its position) and is zeroed after the rotation.
+  const __bf16 *in_bh = (const __bf16 *)a.in + b * a.isb + h * a.ish + lanec * 8;
+  bf16x8_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = *(const bf16x8_t *)(in_bh + (int64_t)min(blk * 128 + j * 16 + rsub, a.n - 1) * a.isn);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int tok = blk * 128 + j * 16 + rsub;
     live[j] = tok < a.n;  // a row's 16 lanes agree
-    if (live[j]) {
-      const bf16x8_t v = *(const bf16x8_t *)((const __bf16 *)a.in + b * a.isb +
-                                             (int64_t)tok * a.isn + h * a.ish + lanec * 8);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[j][k] = (float)v[k];
-      float sn[8], cs[8];
-      pro::lane_angles(a.pos + 3 * tok, theta, axis, sn, cs);
-      pro::norm_rope_row<D>(x[j], lanec, a.gamma, a.eps, sn, cs);
-      if (a.kind == 1) {
+    for (int k = 0; k < 8; ++k) x[j][k] = (float)v[j][k];
+    float sn[8], cs[8];
+    pro::lane_angles(a.pos + 3 * min(tok, a.n - 1), theta, axis, sn, cs);
+    pro::norm_rope_row<D>(x[j], lanec, gam, a.eps, sn, cs);
+    if (a.kind == 1) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[j][k] -= m[k];
-      }
+      for (int k = 0; k < 8; ++k) x[j][k] -= m[k];
+    }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[j][k]));
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) x[j][k] = 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      x[j][k] = live[j] ? x[j][k] : 0.0f;
+      amax = fmaxf(amax, fabsf(x[j][k]));
     }
   }
   if (a.kind == 0 && a.lse && a.mean) {
