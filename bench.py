@@ -538,8 +538,8 @@ def main():
         summarize_rocprof(args.summarize_rocprof, os.path.join(ROOT, "profiles"))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the attention "
-              "shards by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the attention "
+              "would shard by head). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import fa_workloads as W
