@@ -273,3 +273,50 @@ def test_lowbit_stream_through_driver():
         G.compare_sampled(c, {TGT: (G.host(out["o_tgt"])[0], G.host(out["lse_tgt"])[0])},
                           n_rows=32, what="lowbit stream chunk %d" % ch)
     assert s.state() == (18, 6)
+
+
+BATCH_CASES = [
+    # seed, T, C, H, cs, window, cache, refs, t0, query rows
+    (70, 160, 3, 2, 0, 0, 0, [96, 64], [0, 1], 7),   # bidirectional, all query kinds
+    (72, 50, 3, 2, 9, 4, 5, [20], [0], 1),           # streaming, the ring wraps
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=["b%d" % c[0] for c in BATCH_CASES])
+def test_lowbit_batch2_matches_single_calls(case):
+    """Batch 2 through the quantiser and the attention kernel: key means, scales, codes, O and
+    LSE of each batch entry equal those of the same inputs run as a batch-1 call (every
+    statistic is per (batch, head))."""
+    seed, T, C, H, cs, win, cap, refs, t0s, qr = case
+    G.say("case: low-bit batch 2 %s" % (case,))
+    runs = [LowbitRun(lowbit_call(seed + b, T, C, H, cs, win, cap, refs, t0s, qr)) for b in range(2)]
+    single = []
+    for r in runs:
+        r.quantize()
+        single.append(r.attend())
+    c0 = runs[0].c
+    d = c0.desc()
+    d.batch = 2
+    L = B.fa_layout_build(d, c0.ring_first)
+    cat = lambda f: {n: torch.cat([f(runs[0])[n], f(runs[1])[n]]) for n in f(runs[0])}
+    inp = cat(lambda r: r.inp)
+    codes = {n: torch.zeros_like(x) for n, x in cat(lambda r: r.codes).items()}
+    scales = {n: torch.zeros_like(x) for n, x in cat(lambda r: r.scales).items()}
+    out = {n: torch.zeros_like(x) for n, x in cat(lambda r: r.out).items()}
+    k_mean = torch.zeros((2, H, 128), dtype=torch.float32, device="cuda")
+    v_absmax = torch.zeros((2, H), dtype=torch.float32, device="cuda")
+    lses = {n: x for n, x in out.items() if n.startswith("lse_")}
+    B.fa_quantize_lowbit(L, B.make_io(inp), B.make_io({**codes, **lses, "k_mean": k_mean,
+                                                       "v_absmax": v_absmax}, scales))
+    B.fa_attn_fwd(L, B.make_io({**codes, **out, "v_absmax": v_absmax}, scales))
+    torch.cuda.synchronize()
+    for b, r in enumerate(runs):
+        assert torch.equal(k_mean[b], r.k_mean[0]), b
+        assert torch.equal(v_absmax[b], r.v_absmax[0]), b
+        for n in r.codes:
+            assert torch.equal(codes[n][b], r.codes[n][0]), (b, n)
+            assert torch.equal(scales[n][b], r.scales[n][0]), (b, n)
+        for k, (o, lse) in single[b].items():
+            nm = G.KIND_NAMES[k]
+            assert np.array_equal(G.host(out["o_" + nm])[b], o), (b, nm)
+            assert np.array_equal(G.host(out["lse_" + nm])[b], lse), (b, nm)

@@ -223,12 +223,14 @@ def test_run_to_run_deterministic():
         assert np.array_equal(a[k][0], b[k][0]) and np.array_equal(a[k][1], b[k][1])
 
 
-def test_strided_and_batched_inputs():
-    """Q/K/V as views into packed [B, N, 3, H, D] buffers, batch 2: same as separate calls."""
-    G.say("case: strided views and batch 2")
+@pytest.mark.parametrize("block_rows", [128, 256], ids=["bm128", "bm256"])
+def test_strided_and_batched_inputs(block_rows):
+    """Q/K/V as views into packed [B, N, 3, H, D] buffers, batch 2: same as separate calls, with
+    either bf16 kernel."""
+    G.say("case: strided views and batch 2, block_rows %d" % block_rows)
     T, C, H, D = 40, 3, 2, 128
     calls = [G.random_call(30 + b, T, C, H, D, "bf16", ref_tokens=[24], ref_t0=[1],
-                           query_rows=7) for b in range(2)]
+                           query_rows=7, block_rows=block_rows) for b in range(2)]
     N = C * T
     packed = {}
     for name, src in (("tgt", lambda c: (c.q[TGT], c.k_hist, c.v_hist)),
@@ -243,7 +245,8 @@ def test_strided_and_batched_inputs():
         rows = p.shape[1]
         t["o_" + name] = torch.zeros((2, rows, H, D), dtype=torch.bfloat16, device="cuda")
         t["lse_" + name] = torch.zeros((2, H, rows), dtype=torch.float32, device="cuda")
-    d = B.make_desc(C, T, H, D, batch=2, ref_tokens=[24], ref_t0=[1], query_rows=7)
+    d = B.make_desc(C, T, H, D, batch=2, ref_tokens=[24], ref_t0=[1], query_rows=7,
+                    block_rows=block_rows)
     B.fa_attn_fwd(B.fa_layout_build(d), B.make_io(t))
     torch.cuda.synchronize()
     for b, c in enumerate(calls):
