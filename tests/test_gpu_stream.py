@@ -158,3 +158,40 @@ def test_stream_with_sink_frames():
         want = run.k_all[f // 3][(f % 3) * w.T:(f % 3 + 1) * w.T]
         assert np.array_equal(kr[s * w.T:(s + 1) * w.T], want), f
     assert run.s.state() == (36, 30)
+
+
+APPEND_CASES = [  # dtype, head_dim, batch, T, H, ring frames, sink frames, first frame, frames, pad
+    ("bf16", 128, 1, 37, 3, 5, 0, 3, 3, 0),   # frames 3, 4, 5 -> slots 3, 4, 0 (wraps)
+    ("bf16", 64, 2, 20, 4, 6, 2, 7, 3, 8),    # 2 sink slots; frames 7..9 -> slots 3..5; padded heads
+    ("f32", 128, 2, 9, 2, 4, 1, 0, 4, 0),     # 32 pieces a row; frame 0 into the sink slot
+    ("f32", 64, 1, 16, 5, 3, 0, 10, 2, 4),    # frames 10, 11 -> slots 1, 2; padded heads
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES,
+                         ids=["%s_d%d_b%d" % (c[0], c[1], c[2]) for c in APPEND_CASES])
+def test_ring_append_layouts(case):
+    """fa_ring_append is pure data movement: the ring after the call equals the ring before with
+    each appended frame's tokens in its slot (a sink frame in its own slot, the others cycling
+    through the remaining slots), padding between heads untouched, for both element sizes,
+    head_dim 64 and 128 and batch 2."""
+    dt, D, nb, T, H, cap, sink, f0, nf, pad = case
+    G.say("case: ring append %s" % (case,))
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(D + 7 * T + nb)
+    full = lambda n: torch.randn((nb, n, H, D + pad), generator=g).to(tdt).cuda()
+    rings = [full(cap * T), full(cap * T)]
+    chunks = [full(nf * T), full(nf * T)]
+    before = [r.clone() for r in rings]
+    d = B.make_desc(nf, T, H, D, batch=nb, cache_frames=cap, sink_frames=sink,
+                    dtype=B.FA_F32 if dt == "f32" else B.FA_BF16)
+    B.fa_ring_append(d, rings[0][..., :D], rings[1][..., :D], chunks[0][..., :D],
+                     chunks[1][..., :D], f0, nf)
+    torch.cuda.synchronize()
+    for r, b0, ch in zip(rings, before, chunks):
+        want = b0.clone()
+        for fi in range(nf):
+            gf = f0 + fi
+            slot = gf if gf < sink else sink + (gf - sink) % (cap - sink)
+            want[:, slot * T:(slot + 1) * T, :, :D] = ch[:, fi * T:(fi + 1) * T, :, :D]
+        assert torch.equal(r, want)
