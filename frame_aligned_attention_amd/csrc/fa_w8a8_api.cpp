@@ -17,12 +17,13 @@ fa_status check_shape(int32_t rows, int32_t cols, const char *what) {
 }
 
 // leading dimension in elements of size es: at least cols, rows 16-byte aligned, offsets of a
-// 128-row tile within 2^31 bytes
+// 256-row tile within 2^31 bytes
 fa_status check_ld(int64_t ld, int32_t cols, int es, const char *what) {
   if (ld < cols) return fail(FA_ERR_INVALID, std::string(what) + ": leading dimension < columns");
   if ((ld * es) % 16) return fail(FA_ERR_INVALID, std::string(what) + ": rows not 16-byte aligned");
-  if (ld * es >= (int64_t(1) << 24))
-    return fail(FA_ERR_UNSUPPORTED, std::string(what) + ": leading dimension of 2^24 bytes or more");
+  // the GEMM addresses a 256-row operand tile with 32-bit offsets: 256 rows stay below 2^31 bytes
+  if (ld * es >= (int64_t(1) << 23))
+    return fail(FA_ERR_UNSUPPORTED, std::string(what) + ": leading dimension of 2^23 bytes or more");
   return FA_OK;
 }
 

@@ -298,7 +298,8 @@ fa_status fa_qk_norm_rope_quant(const fa_tensor *in, const fa_tensor *codes, con
  * calls are asynchronous on `stream` and allocate nothing.  Argument errors
  * (NULL, misaligned base or rows -- bases 16-byte aligned, rows a multiple of
  * 16 bytes --, k or n not multiples of 128, ld < columns) return
- * FA_ERR_INVALID before any launch; FA_ERR_HIP on a failed launch.
+ * FA_ERR_INVALID before any launch; a row of 2^23 bytes or more returns
+ * FA_ERR_UNSUPPORTED; FA_ERR_HIP on a failed launch.
  *
  * fa_w8a8_quantize_act: x bf16 [m][ld_x] -> xq int8 [m][ld_xq] and sx fp32
  * with the scale of row i, K-block b at sx[b * ld_sx + i] (ld_sx >= m).

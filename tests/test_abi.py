@@ -191,3 +191,27 @@ def test_stream_state_and_seek():
     s.set_refs([16, 8], [0, 14])
     with pytest.raises(B.FaError):
         s.set_refs([1] * 9, [0] * 9)
+
+
+def test_w8a8_gemm_argument_checks():
+    """fa_w8a8_gemm rejects bad shapes, alignment and leading dimensions on the host (every case
+    returns before a launch; the pointers are aligned stand-ins that are never dereferenced)."""
+    P = C.c_void_p
+    ptr = 0x10000
+    base = dict(xq=ptr, ld_xq=256, sx=ptr, ld_sx=64, wq=ptr, ld_wq=256, sw=ptr, m=64, n=128,
+                k=256, y=ptr, ld_y=128)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return B.lib.fa_w8a8_gemm(P(a["xq"]), a["ld_xq"], P(a["sx"]), a["ld_sx"], P(a["wq"]),
+                                  a["ld_wq"], P(a["sw"]), a["m"], a["n"], a["k"], P(a["y"]),
+                                  a["ld_y"], None)
+
+    assert call(m=0) == B.FA_OK and call(n=0) == B.FA_OK  # nothing to do
+    for kw in (dict(n=100), dict(k=200), dict(k=0), dict(m=-1), dict(ld_xq=255),
+               dict(ld_xq=264), dict(ld_wq=200), dict(ld_y=120), dict(ld_sx=63),
+               dict(xq=ptr + 8), dict(y=ptr + 4), dict(sx=ptr + 2), dict(xq=0)):
+        assert call(**kw) == B.FA_ERR_INVALID, kw
+    # a 256-row activation tile must stay within 32-bit offsets
+    assert call(ld_xq=1 << 23, k=256) == B.FA_ERR_UNSUPPORTED
+    assert call(ld_y=1 << 22, n=128) == B.FA_ERR_UNSUPPORTED  # 2^23 bytes of bf16
