@@ -150,6 +150,8 @@ static fa_status ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
   if (nonsink > (int64_t)d->cache_frames - d->sink_frames)
     return fail(FA_ERR_INVALID, "more non-sink frames than the ring's cycling slots");
   if (frames == 0) return FA_OK;
+  if (d->batch > 32767 || (int64_t)frames * d->tokens_per_frame * d->heads > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "append: batch above 32767 or 2^31 (token, head) rows");
   const int es = d->dtype == FA_F32 ? 4 : 2;
   const fa_tensor *t[4] = {k_ring, v_ring, k_chunk, v_chunk};
   const char *nm[4] = {"k_ring", "v_ring", "k_chunk", "v_chunk"};

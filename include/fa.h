@@ -245,8 +245,9 @@ fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *o
  * k_chunk/v_chunk -- absolute frames first_frame .. first_frame+frames-1 --
  * into their ring slots (see fa_io; sink frames keep slots 0 ..
  * sink_frames-1).  At most cache_frames - sink_frames non-sink frames per
- * call, else FA_ERR_INVALID.  Element type from d->dtype (FA_LOWBIT rings
- * hold bf16 and are quantised per call).  Asynchronous.
+ * call, else FA_ERR_INVALID.  Batch above 32767, or 2^31 or more (token, head)
+ * rows in one append, return FA_ERR_UNSUPPORTED.  Element type from d->dtype
+ * (FA_LOWBIT rings hold bf16 and are quantised per call).  Asynchronous.
  */
 fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const fa_tensor *v_ring,
                          const fa_tensor *k_chunk, const fa_tensor *v_chunk, int32_t first_frame,

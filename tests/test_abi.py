@@ -171,6 +171,9 @@ def test_ring_append_rejects_bad_args_on_host():
     d = desc(sink_frames=5)  # more sink frames than slots
     assert B.lib.fa_ring_append(C.byref(d), C.byref(t), C.byref(t), C.byref(t), C.byref(t), 0, 0,
                                 None) == B.FA_ERR_INVALID
+    d = desc(batch=40000)  # the launch grid holds tensor and batch in its y dimension
+    assert B.lib.fa_ring_append(C.byref(d), C.byref(t), C.byref(t), C.byref(t), C.byref(t), 0, 1,
+                                None) == B.FA_ERR_UNSUPPORTED
 
 
 def test_stream_state_and_seek():
