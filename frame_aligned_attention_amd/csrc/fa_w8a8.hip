@@ -14,7 +14,8 @@
 // is one register per 32-row tile and the weight scale is uniform per workgroup.  Operand tiles
 // go straight from HBM into a 3-stage LDS ring (direct loads, bounds-checked descriptors
 // zero-fill rows past m), rows XOR-swizzled in 16-byte chunks for conflict-free MFMA operand
-// reads; a K-block's loads have two steps to land.
+// reads; a K-block's loads have two steps to land.  The two waves on each SIMD ping-pong: one
+// multiplies a block while the other dequantises.
 #include "fa_device.h"
 
 namespace fa {
@@ -273,19 +274,26 @@ __global__ void __launch_bounds__(512, 1) w8a8_gemm_kernel(const W8GemmArgs a) {
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Step kb: scales of block kb, then the tiles of block kb+2 (in that order, so that waiting
-  // for the scales leaves the tile loads in flight); then the MFMAs of block kb (stage kb % 3)
-  // and their dequantisation (the other wave on the SIMD covers the wait for the products).  At
-  // the end each wave waits for all but this step's tile loads (block kb+1 has landed) and the
-  // barrier publishes them.  The waits are s_waitcnt builtins, which the compiler's own wait
-  // counting sees (an inline-asm wait is opaque to it, and it then inserts full waits).
+  // Ping-pong.  Waves 0-3 (group A, n rows 0..63) and 4-7 (group B, n rows 64..127) pair up
+  // on the four SIMDs.  Step kb has two slots: in the first, A multiplies block kb while B
+  // dequantises block kb-1; in the second, A dequantises kb while B multiplies it.  A barrier
+  // (no fence) hands the slots over; the step's last barrier publishes block kb+1.  Each group
+  // keeps one set of int32 products; A's live within a step, B's across the publish.
+  // At the start of a step every wave issues the scales of its block and its share of the tiles
+  // of block kb+2 (scales first, so that waiting for them leaves the tile loads in flight).  At
+  // the step's end each wave waits for all but the newest six loads (block kb+1 has landed).  The
+  // waits are s_waitcnt builtins, which the compiler's own wait counting sees (an inline-asm
+  // wait is opaque to it, and it then inserts full waits).
   i32x16_t part[2][2];
-  auto step = [&](int kb, const char *xbuf, const char *wbuf, char *xnext, char *wnext) {
-    float s[2];
-    load_sx(kb, s);
+  const bool grp_a = wn == 0;
+  auto handover = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    issue(kb + 2, xnext, wnext);
-    const float swk = swp[kb];
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfma_slot = [&](const char *xbuf, const char *wbuf) {
     mfmas(xbuf, wbuf, part);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS: operands of k-step 0
 #pragma unroll
@@ -293,32 +301,88 @@ __global__ void __launch_bounds__(512, 1) w8a8_gemm_kernel(const W8GemmArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (i % 4 == 0 && i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS
     }
-    dequant(part, s, swk);
+  };
+  auto end_step = [&]() {
     static_assert(XLOADS + WLOADS == 6, "wait count below");
     __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6), a wait the compiler's counter sees
     publish();
+  };
+  // Group A, step kb: MFMAs of block kb (stage kb % 3), then their dequantisation.
+  auto stepA = [&](int kb, const char *xbuf, const char *wbuf, char *xnext, char *wnext) {
+    float s[2];
+    load_sx(kb, s);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 2, xnext, wnext);
+    const float swk = swp[kb];
+    mfma_slot(xbuf, wbuf);
+    handover();
+    dequant(part, s, swk);
+    end_step();
+  };
+  // Group B, iteration kb: the second slot of step kb (MFMAs of block kb), its publish, the start
+  // of step kb+1 (scales of block kb+1 into sn; tiles of block kb+3 into the stage just
+  // multiplied) and the first slot of step kb+1 (dequantisation of block kb with scales sc).
+  // Products made and consumed in one iteration keep one register set.
+  auto iterB = [&](int kb, char *xbuf, char *wbuf, const float (&sc)[2], float (&sn)[2]) {
+    mfma_slot(xbuf, wbuf);
+    end_step();
+    load_sx(kb + 1, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + 3, xbuf, wbuf);
+    dequant(part, sc, swp[kb]);
   };
 
   issue(0, xs0, ws0);
   issue(1, xs1, ws1);
   __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6): block 0
   publish();
-  // Unrolled so every stage is a compile-time name (the compiler then knows which LDS array a
-  // load in flight writes).  At the loop head it still waits for the newest loads, so six steps
-  // per iteration rather than three halve that cost.
-  for (int kb = 0;;) {
-    step(kb, xs0, ws0, xs2, ws2);
-    if (++kb >= kbt) break;
-    step(kb, xs1, ws1, xs0, ws0);
-    if (++kb >= kbt) break;
-    step(kb, xs2, ws2, xs1, ws1);
-    if (++kb >= kbt) break;
-    step(kb, xs0, ws0, xs2, ws2);
-    if (++kb >= kbt) break;
-    step(kb, xs1, ws1, xs0, ws0);
-    if (++kb >= kbt) break;
-    step(kb, xs2, ws2, xs1, ws1);
-    if (++kb >= kbt) break;
+  // Both loops are unrolled so every stage is a compile-time name (the compiler then knows which
+  // LDS array a load in flight writes; at a loop head it still waits for the newest loads, so
+  // six steps per iteration rather than three halve that cost).  Both pass the same barriers:
+  // 1 + 2 kbt.
+  if (grp_a) {
+    for (int kb = 0;;) {
+      stepA(kb, xs0, ws0, xs2, ws2);
+      if (++kb >= kbt) break;
+      stepA(kb, xs1, ws1, xs0, ws0);
+      if (++kb >= kbt) break;
+      stepA(kb, xs2, ws2, xs1, ws1);
+      if (++kb >= kbt) break;
+      stepA(kb, xs0, ws0, xs2, ws2);
+      if (++kb >= kbt) break;
+      stepA(kb, xs1, ws1, xs0, ws0);
+      if (++kb >= kbt) break;
+      stepA(kb, xs2, ws2, xs1, ws1);
+      if (++kb >= kbt) break;
+    }
+  } else {
+    float sa[2], sb[2];
+    // start of step 0: scales of block 0, tiles of block 2; nothing to dequantise in its first
+    // slot
+    load_sx(0, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(2, xs2, ws2);
+    handover();
+    for (int kb = 0;;) {
+      iterB(kb, xs0, ws0, sa, sb);
+      if (++kb >= kbt) break;
+      handover();
+      iterB(kb, xs1, ws1, sb, sa);
+      if (++kb >= kbt) break;
+      handover();
+      iterB(kb, xs2, ws2, sa, sb);
+      if (++kb >= kbt) break;
+      handover();
+      iterB(kb, xs0, ws0, sb, sa);
+      if (++kb >= kbt) break;
+      handover();
+      iterB(kb, xs1, ws1, sa, sb);
+      if (++kb >= kbt) break;
+      handover();
+      iterB(kb, xs2, ws2, sb, sa);
+      if (++kb >= kbt) break;
+      handover();
+    }
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the workgroup
 
