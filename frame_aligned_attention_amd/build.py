@@ -30,9 +30,19 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+def file_flags(src: str) -> list:
+    """Extra flags a source asks for on a `// build-flags:` line among its first 40 lines, so
+    that the source text (and its hash) covers how it is compiled."""
+    with open(src) as f:
+        for _, line in zip(range(40), f):
+            if line.startswith("// build-flags:"):
+                return line.split(":", 1)[1].split()
+    return []
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + file_flags(src) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
