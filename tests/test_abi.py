@@ -218,3 +218,12 @@ def test_w8a8_gemm_argument_checks():
     # a 256-row activation tile must stay within 32-bit offsets
     assert call(ld_xq=1 << 23, k=256) == B.FA_ERR_UNSUPPORTED
     assert call(ld_y=1 << 22, n=128) == B.FA_ERR_UNSUPPORTED  # 2^23 bytes of bf16
+
+
+def test_per_source_build_flags():
+    """A source's `// build-flags:` line is what the build passes for it (and it sits in the
+    hashed source text); only the bf16 attention file asks for any."""
+    from frame_aligned_attention_amd import build as fb
+    flags = {os.path.basename(s): fb.file_flags(s) for s in fb.sources()}
+    assert flags["fa_attn_bf16.hip"] == ["-fno-honor-nans"]
+    assert all(v == [] for k, v in flags.items() if k != "fa_attn_bf16.hip")
