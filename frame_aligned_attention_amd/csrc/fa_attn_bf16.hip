@@ -562,7 +562,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   f32x16_t oacc[Cfg::DB];
 #pragma unroll
   for (int i = 0; i < Cfg::DB; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
+  // finite start: the first tile with any visible key always raises it, so -m_run is the exp
+  // offset from then on with no test for -inf (a row with no visible key keeps l = 0)
+  float m_run = -1e30f;
   float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in four chains
   const float c = a.c;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -679,7 +681,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
 #pragma unroll
         for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
       }
-      const float mneg = m_run == -__builtin_inff() ? 0.0f : -m_run;
+      const float mneg = -m_run;
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
