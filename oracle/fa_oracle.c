@@ -150,12 +150,14 @@ static void sum_fn(const float *k, const float *v, void *vctx) {
 
 static int one_row(const fa_oracle_problem *p, int kind, int h, int row, float *o, float *lse) {
   const int D = p->D;
-  const float *q = query_ptr(p, kind) + ((long)row * p->H + h) * D;
+  const float *q;
   max_ctx mc;
   sum_ctx sc;
   double acc[1024];
   int d, rc;
   if (D > 1024) return -2;
+  if (kind < 0 || kind > 2 || h < 0 || h >= p->H || row < 0 || row >= rows_of(p, kind)) return -2;
+  q = query_ptr(p, kind) + ((long)row * p->H + h) * D;
   mc.q = q; mc.D = D; mc.scale = p->scale; mc.m = 0.0; mc.n = 0;
   rc = for_visible_keys(p, kind, row, h, max_fn, &mc);
   if (rc) return rc;

@@ -12,6 +12,7 @@ What pins what:
   F = 1             plain unmasked attention (library routine)
   two keys          closed form sigmoid -> the scale, base e, LSE formula
   Q = 0             O = mean of the visible V, LSE = ln(#visible) exactly
+  rows == full      the single-row entry point returns the full call's slices bit for bit
   V = 1             rows of probabilities sum to one
   perturbation      each "only" of the rule: bit-identical outputs
   permutation       key order inside a frame does not matter
@@ -300,6 +301,35 @@ def pin_q_zero(lib):
                 for h in range(p.H):
                     close(res[kind][1][h, row], math.log(n), 1e-7, "Q=0 LSE")
                     close(res[kind][0][row, h], visible_mean(p, kind, row, h), 1e-6, "Q=0 O")
+
+
+def pin_rows_match_full(lib):
+    """fa_oracle_attn_rows (the entry point behind every sampled full-size check) returns, for
+    each (kind, head, row) it is asked for, exactly the slice fa_oracle_attn writes for that
+    row: same O bits, same LSE bits, over every layout (sink and gated ones included).  H = 3
+    and rows both above and below H make a swapped head/row index visible."""
+    g = np.random.default_rng(11)
+    for i, lay in enumerate(LAYOUTS):
+        a = layout_args(lay)
+        p = rand_problem(300 + i, a["T"], a["C"], 3, 8, a["cs"], a["window"], a["hist_first"],
+                         a["ref_tokens"], a["ref_t0"], sink=a["sink"])
+        full = O.attn(p, lib=lib)
+        kk, hh, rr = [], [], []
+        for kind in (TGT, SRC, REF):
+            n = p.rows(kind)
+            if n == 0:
+                continue
+            rows = list(range(n)) if n <= 8 else sorted(set(g.integers(0, n, 8).tolist()) |
+                                                          {0, n - 1})
+            for r in rows:
+                for h in range(p.H):
+                    kk.append(kind); hh.append(h); rr.append(r)
+        order = g.permutation(len(kk))
+        kk, hh, rr = [kk[j] for j in order], [hh[j] for j in order], [rr[j] for j in order]
+        o, lse = O.attn_rows(p, kk, hh, rr, lib=lib)
+        for j, (kind, h, r) in enumerate(zip(kk, hh, rr)):
+            assert np.array_equal(o[j], full[kind][0][r, h]), ("rows O", i, kind, h, r)
+            assert np.array_equal(lse[j], full[kind][1][h, r]), ("rows LSE", i, kind, h, r)
 
 
 def pin_ones_v(lib):
@@ -644,7 +674,7 @@ def pin_norm_rope(lib):
 
 
 ALL_PINS = [pin_golden_masks, pin_bruteforce, pin_f1_full_attention, pin_two_keys,
-            pin_large_scores, pin_q_zero,
+            pin_large_scores, pin_q_zero, pin_rows_match_full,
             pin_ones_v, pin_perturbations, pin_permutation, pin_split_merge,
             pin_streaming_consistency, pin_sink, pin_smoothing, pin_quant_int8, pin_quant_e4m3, pin_kmean, pin_w8a8_quant, pin_w8a8_gemm,
             pin_norm_rope]

@@ -37,6 +37,9 @@ MUTANTS = {
     "no normalisation": ("o[d] = (float)(acc[d] / sc.l);", "o[d] = (float)(acc[d]);"),
     "relative query frame": ("const int qframe = kind == FAO_REF ? -1 : p->cs + row / T;",
                              "const int qframe = kind == FAO_REF ? -1 : row / T;"),
+    "rows: head and row swapped": (
+        "const int rc = one_row(p, kind[i], head[i], row[i], o + (long)i * p->D, lse + i);",
+        "const int rc = one_row(p, kind[i], row[i], head[i], o + (long)i * p->D, lse + i);"),
     "max not updated": ("if (c->n == 0 || s > c->m) c->m = s;", "if (c->n == 0) c->m = s;"),
     "int8 truncation": ("float r = nearbyintf(y);", "float r = truncf(y);"),
     "int8 ties away": ("float r = nearbyintf(y);", "float r = roundf(y);"),
