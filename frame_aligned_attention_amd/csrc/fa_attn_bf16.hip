@@ -74,20 +74,27 @@ struct Bf16Cfg {
   // again hits 16 distinct slots (with D = 64 two rows share a slot).
   __device__ static int ksw(int r) { return r & (CH - 1); }
   __device__ static int vsw(int r) { return (4 * r) & (CH - 1); }
+  // V in the ping-pong kernel (16x16x32 products): a transposing read group of 16 lanes takes
+  // rows 4g..4g+3 at two consecutive logical chunks; chunk c of row r lives at c ^ 2(r % 8),
+  // so the eight rows a half wave reads land on eight distinct chunk pairs (with D = 64, rows
+  // r and r + 4 share a pair).
+  __device__ static int vsw16(int r) { return (2 * r) & (CH - 1) & 14; }
 };
 
 // Where each lane's direct loads of a tile land and which bytes of the tile's rows they fetch:
 // load j of wave w writes LDS chunks [(4j + w)*64, +64) of the tile, lane i chunk
 // (4j + w)*64 + i, i.e. row row0 + j*RSTEP at logical chunk lcb/16 of that row.  RSTEP is a
 // multiple of CH, so the swizzle (a function of the row modulo CH) is the same for every j.
-template <int D, bool IS_V>
+// SW: 0 = K, 1 = V of the 4-wave kernel, 2 = V of the ping-pong kernel.
+template <int D, int SW>
 __device__ __forceinline__ void load_map(int w, int lane, int &row0, int &lcb) {
   using Cfg = Bf16Cfg<D>;
-  static_assert(Cfg::RSTEP % Cfg::CH == 0, "swizzle must not depend on the load index");
+  static_assert(Cfg::RSTEP % Cfg::CH == 0 && Cfg::RSTEP % 8 == 0,
+                "swizzle must not depend on the load index");
   const int p = w * 64 + lane;
   row0 = p / Cfg::CH;
   const int pc = p % Cfg::CH;
-  const int lc = pc ^ (IS_V ? Cfg::vsw(row0) : Cfg::ksw(row0));
+  const int lc = pc ^ (SW == 2 ? Cfg::vsw16(row0) : SW == 1 ? Cfg::vsw(row0) : Cfg::ksw(row0));
   lcb = lc * 16;
 }
 
@@ -149,8 +156,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
   }
   // direct-load row and column of this lane's first load (K and V layouts differ)
   int krow0, kcb0, vrow0, vcb0;
-  load_map<D, false>(wave, lane, krow0, kcb0);
-  load_map<D, true>(wave, lane, vrow0, vcb0);
+  load_map<D, 0>(wave, lane, krow0, kcb0);
+  load_map<D, 1>(wave, lane, vrow0, vcb0);
 
   // ---- tile cursors over the flattened (range, 64-key tile) sequence.  Each cursor keeps the
   // fields of its current range (and, for the load cursors, the (batch, head) base of the
@@ -436,11 +443,28 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 // while the other wave's exp work issues beside it.  Group A also issues the
 // direct loads of the pair's K and V tiles, one every few MFMAs of its matrix
 // phase; they have the pair's second slot to land.
+//
+// Its products run on v_mfma_f32_16x16x32_bf16 (16x16 outputs, 32-deep), which
+// sustains a higher share of the matrix core's peak on gfx950 than the 32x32x16
+// form.  Per wave, 32 query rows in two 16-row blocks qb and 64 keys in four
+// 16-key blocks kb:
+//   S^T[kb][qb] (16 keys x 16 queries) = K_kb . Q_qb^T, four 32-channel k-steps;
+//     lane l holds query qb*16 + l%16 and keys kb*16 + 4*(l/16) + r, r = 0..3,
+//     so a query's 64 scores sit in the four lanes l%16 + {0,16,32,48}: 16 in
+//     each, reduced in-lane, then by v_permlane32_swap and v_permlane16_swap.
+//   O^T[cb][qb] (16 channels x 16 queries) += V^T . P^T over two 32-key steps t;
+//     the B operand of step t is lane l's p of key blocks 2t and 2t+1 (keys
+//     32t + 4g + r and 32t + 16 + 4g + r, g = l/16), so P never leaves its
+//     lane; the A operand takes the same keys of channel cb*16 + l%16 from two
+//     transposing LDS reads.
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) {
   using Cfg = Bf16Cfg<D>;
   constexpr int BN = Cfg::BN, ROWB = Cfg::ROWB, TILEB = Cfg::TILEB;
+  constexpr int KS = D / 32;   // 32-channel k-steps of S^T
+  constexpr int CB = D / 16;   // 16-channel blocks of O^T
   constexpr float kThr = 8.0f;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
   // LDS: two K and two V tile buffers.  Separate arrays (not one array indexed by buffer) let
   // the compiler see that direct loads into one buffer never alias reads of another, so it
   // does not wait for in-flight prefetches before every LDS read.
@@ -457,48 +481,54 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // the wave index is uniform per wave; say so, since it feeds M0 (LDS address of direct loads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool grp_a = wave < 4;  // group A: matrix phase first in every slot pair
-  const int lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int T = a.T;
   // a wave whose 32 rows all lie past the tile's end only loads and keeps step
   const bool wlive = wave * 32 < tile.rows;
 
-  // ---- Q (B operand of S^T): lane holds query row l32 of its wave, channels ds*16 + 8*hl + 0..7
-  const int qloc = wave * 32 + l32;
-  const bool qvalid = qloc < tile.rows;
-  const int qrow = tile.row0 + qloc;
-  bf16x8_t qreg[Cfg::DS];
+  // ---- Q (B operand of S^T): lane holds query row l16 of block qb, channels ks*32 + 8*g4 + 0..7
+  bf16x8_t qreg[2][KS];
+  int fq[2];  // row frame relative to the chunk (target and source rows)
+  bool qvalid[2];
+  int qrow[2];
   {
     const Seg qs = a.q[tile.q_kind];
-    const __bf16 *qp = (const __bf16 *)qs.p + b * qs.sb + (int64_t)qrow * qs.sn + h * qs.sh;
 #pragma unroll
-    for (int ds = 0; ds < Cfg::DS; ++ds)
-      qreg[ds] = qvalid ? *(const bf16x8_t *)(qp + ds * 16 + 8 * hl) : bf16x8_t{};
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qloc = wave * 32 + qb * 16 + l16;
+      qvalid[qb] = qloc < tile.rows;
+      qrow[qb] = tile.row0 + qloc;
+      fq[qb] = qrow[qb] / T;
+      const __bf16 *qp =
+          (const __bf16 *)qs.p + b * qs.sb + (int64_t)qrow[qb] * qs.sn + h * qs.sh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qreg[qb][ks] = qvalid[qb] ? *(const bf16x8_t *)(qp + ks * 32 + 8 * g4) : bf16x8_t{};
+    }
   }
-  const int fq = qrow / T;  // row frame relative to the chunk (target and source rows)
 
   // ---- per-lane constants of the LDS reads
-  // K (A operand of S^T): row kb*32 + l32, logical chunk 2*ds + hl.
-  int koff[Cfg::DS];
+  // K (A operand of S^T): row kb*16 + l16, logical chunk 4*ks + g4 (kb moves the row by 16,
+  // which leaves the swizzle alone: an immediate offset).
+  int koff[KS];
 #pragma unroll
-  for (int ds = 0; ds < Cfg::DS; ++ds)
-    koff[ds] = l32 * ROWB + (((2 * ds + hl) ^ Cfg::ksw(l32)) * 16);
-  // V (A operand of O^T via the transposing read): lane i = 4s + av of 16-lane group g reads
-  // row ks*16 + r*8 + 4*(g/2) + s, channels db*32 + (g%2)*16 + 4*av .. +3.
-  int voff[Cfg::DB];
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = l16 * ROWB + (((4 * ks + g4) ^ Cfg::ksw(l16)) * 16);
+  // V (A operand of O^T via the transposing read): the 16 lanes of group g4 read key rows
+  // 4*g4 + (l16 >> 2) (+ 32t, + 16 for the second read) at channels cb*16 + 4*(l16 & 3) .. +3;
+  // lane l16 of the group then holds those four keys of channel cb*16 + l16.
+  int voff[CB];
   {
-    const int i = lane & 15, g = lane >> 4;
-    const int s = i >> 2, av = i & 3, hv = g >> 1, gh = g & 1;
-    const int vrow = 4 * hv + s;
+    const int vrow = 4 * g4 + (l16 >> 2);
 #pragma unroll
-    for (int db = 0; db < Cfg::DB; ++db) {
-      const int lc = db * 4 + gh * 2 + (av >> 1);
-      voff[db] = vrow * ROWB + ((lc ^ Cfg::vsw(vrow)) * 16) + (av & 1) * 8;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int lc = 2 * cb + ((l16 & 3) >> 1);
+      voff[cb] = vrow * ROWB + ((lc ^ Cfg::vsw16(vrow)) * 16) + (l16 & 1) * 8;
     }
   }
   // direct-load row and column of this lane's first load (K and V layouts differ)
   int krow0, kcb0, vrow0, vcb0;
-  load_map<D, false>(wave, lane, krow0, kcb0);
-  load_map<D, true>(wave, lane, vrow0, vcb0);
+  load_map<D, 0>(wave, lane, krow0, kcb0);
+  load_map<D, 2>(wave, lane, vrow0, vcb0);
 
   // ---- tile cursors over the flattened (range, 64-key tile) sequence.  Each cursor keeps the
   // fields of its current range (and, for the load cursors, the (batch, head) base of the
@@ -559,38 +589,41 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     for (int j = 0; j < Cfg::LOADS; ++j) load_one(rs, o, c.sn2, buf, j);
   };
 
-  f32x16_t oacc[Cfg::DB];
+  f32x4_t oacc[CB][2];
 #pragma unroll
-  for (int i = 0; i < Cfg::DB; ++i) oacc[i] = f32x16_t{};
+  for (int cb = 0; cb < CB; ++cb) oacc[cb][0] = oacc[cb][1] = f32x4_t{};
   // finite start: the first tile with any visible key always raises it, so -m_run is the exp
   // offset from then on with no test for -inf (a row with no visible key keeps l = 0)
-  float m_run = -1e30f;
-  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in four chains
+  float m_run[2] = {-1e30f, -1e30f};
+  float l_part[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // row sums, two chains per query block
   const float c = a.c;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};  // S^T of the tile awaiting its softmax
-  u32x4_t pw[4];  // P^T operands of the four 16-key slices, as packed bf16 pairs
+  f32x4_t s[4][2];  // S^T of the tile awaiting its softmax, [kb][qb]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pw[i] = u32x4_t{};
+  for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4_t{};
+  u32x4_t pw[2][2];  // P^T operands [t][qb], as packed bf16 pairs
+#pragma unroll
+  for (int t = 0; t < 2; ++t) pw[t][0] = pw[t][1] = u32x4_t{};
 
-  // S^T = K . Q^T, one k-step, both 32-key halves of the tile
-  auto qk_step = [&](const lds_char *Kl, int ds) {
-    const bf16x8_t a0 = *(const bf16x8_t *)(Kl + koff[ds]);
-    const bf16x8_t a1 = *(const bf16x8_t *)(Kl + 32 * ROWB + koff[ds]);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ds], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ds], s1, 0, 0, 0);
+  // S^T += K . Q^T for key block kb and k-step ks, both query blocks
+  auto qk_step = [&](const lds_char *Kl, int kb, int ks) {
+    const bf16x8_t ka = *(const bf16x8_t *)(Kl + kb * 16 * ROWB + koff[ks]);
+    s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[0][ks], s[kb][0], 0, 0, 0);
+    s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[1][ks], s[kb][1], 0, 0, 0);
   };
-  // O^T += V^T . P^T, one 16-key slice and one 32-channel block
-  auto pv_step = [&](const lds_char *Vl, int ks, int db) {
-    const lds_char *src = Vl + ks * 16 * ROWB + voff[db];
+  // O^T += V^T . P^T for channel block cb and key step t, both query blocks
+  auto pv_step = [&](const lds_char *Vl, int t, int cb) {
+    const lds_char *src = Vl + t * 32 * ROWB + voff[cb];
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4_t *)(src));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(src + 8 * ROWB));
+        (__attribute__((address_space(3))) s16x4_t *)(src + 16 * ROWB));
     const s16x4_t both[2] = {lo, hi};
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
-    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        av, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[db], 0, 0, 0);
+    oacc[cb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        av, __builtin_bit_cast(bf16x8_t, pw[t][0]), oacc[cb][0], 0, 0, 0);
+    oacc[cb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        av, __builtin_bit_cast(bf16x8_t, pw[t][1]), oacc[cb][1], 0, 0, 0);
   };
 
   // Matrix phase: S of the next tile (K in `kbuf`) and O += V P of this one (V in `vbuf`, P in
@@ -602,10 +635,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   auto matrix_phase = [&](const char *kbuf, const char *vbuf, auto with_loads, const Cur &kc,
                           char *kw, const Cur &vc, char *vw) {
     const lds_char *Kl = (const lds_char *)kbuf, *Vl = (const lds_char *)vbuf;
-    constexpr int NQK = 2 * Cfg::DS, NPV = 4 * Cfg::DB, NL = 2 * Cfg::LOADS;
+    constexpr int NQK = 4 * KS, NPV = 2 * CB, NL = 2 * Cfg::LOADS;  // in pairs of MFMAs
     constexpr int EVERY = (NQK + NPV) / NL;
-    s0 = f32x16_t{};
-    s1 = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4_t{};
     if constexpr (decltype(with_loads)::value) {
       const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kc), vrs = tile_rsrc(vc);
       const uint32_t kof = lane_off(kc, false), vof = lane_off(vc, true);
@@ -614,85 +647,99 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
 #pragma unroll
       for (int j = 0; j < Cfg::LOADS; ++j) load_one(vrs, vof, vc.sn2, vw, j);
     }
+    // k-step major, so the four S accumulators of a query block are never needed back to back
 #pragma unroll
-    for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(Kl, ds);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int kb = 0; kb < 4; ++kb) qk_step(Kl, kb, ks);
 #pragma unroll
-      for (int db = 0; db < Cfg::DB; ++db) pv_step(Vl, ks, db);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read: K operands of k-steps 0, 1
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) pv_step(Vl, t, cb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read: K operands of pairs 0..2
 #pragma unroll
     for (int i = 0; i < NQK + NPV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK, then PV)
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA pair (QK, then PV)
       if constexpr (decltype(with_loads)::value)
         if (i % EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-      // operands four MFMAs ahead: K reads (one per QK MFMA), then V reads (two per PV MFMA)
-      if (i + 4 < NQK)
+      // operands three MFMA pairs ahead: K reads (one per QK pair), then V reads (two per PV pair)
+      if (i + 3 < NQK)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      else if (i + 4 < NQK + NPV)
+      else if (i + 3 < NQK + NPV)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 
-  // Softmax phase of the tile at mask cursor cc, whose scores are in (s0, s1): mask, row max,
-  // (rare) O rescale, P = exp2(c s - m) into pw, row sum.  Advances cc to the next tile.
+  // Softmax phase of the tile at mask cursor cc, whose scores are in s: mask, row max, (rare)
+  // O rescale, P = exp2(c s - m) into pw, row sums.  Advances cc to the next tile.
   auto softmax_phase = [&](Cur &cc) {
     {
-      // mask: s{kb}[i] is key cc.k + kb*32 + (i/4)*8 + 4*hl + i%4 of this lane's query; only
+      // mask: s[kb][qb][r] is key cc.k + kb*16 + 4*g4 + r of query block qb's row; only
       // partial tiles and masked ranges come here
       if (cc.mask != FA_MASK_NONE || cc.k + BN > cc.end) {
-        int klo = cc.begin, khi = cc.end;
-        if (cc.mask == FA_MASK_SAME_FRAME) {
-          klo = max(klo, fq * T);
-          khi = min(khi, (fq + 1) * T);
-        } else if (cc.mask == FA_MASK_GATE && fq < cc.param) {
-          khi = klo;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          int klo = cc.begin, khi = cc.end;
+          if (cc.mask == FA_MASK_SAME_FRAME) {
+            klo = max(klo, fq[qb] * T);
+            khi = min(khi, (fq[qb] + 1) * T);
+          } else if (cc.mask == FA_MASK_GATE && fq[qb] < cc.param) {
+            khi = klo;
+          }
+          // one key at a time (the empty asm keeps the compares from being batched, which
+          // would hold dozens of 64-bit lane masks in scalar registers at once)
+          const uint32_t span = (uint32_t)max(khi - klo, 0);
+          const int base = cc.k + 4 * g4 - klo;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t rel = (uint32_t)(base + kb * 16 + r);
+              float v = s[kb][qb][r];
+              v = rel < span ? v : -__builtin_inff();
+              s[kb][qb][r] = v;
+            }
         }
-        const int base = cc.k + 4 * hl;
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k0i = base + (i >> 2) * 8 + (i & 3);
-          const int k1i = k0i + 32;
-          if (k0i < klo || k0i >= khi) s0[i] = -__builtin_inff();
-          if (k1i < klo || k1i >= khi) s1[i] = -__builtin_inff();
+      for (int qb = 0; qb < 2; ++qb) {
+        // row max: in-lane over the 16 scores as three-way maxima, then across the four lanes
+        // that share the query (l16 + {0, 16, 32, 48})
+        const float m0 = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
+        const float m1 = fmaxf(fmaxf(s[0][qb][3], s[1][qb][0]), s[1][qb][1]);
+        const float m2 = fmaxf(fmaxf(s[1][qb][2], s[1][qb][3]), s[2][qb][0]);
+        const float m3 = fmaxf(fmaxf(s[2][qb][1], s[2][qb][2]), s[2][qb][3]);
+        const float m4 = fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), s[3][qb][2]);
+        float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
+        mx = xhalf_max(mx);
+        mx = x16_max(mx);
+        // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
+        const float mt = mx * c;
+        const bool need = mt > m_run[qb] + kThr;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
+        m_run[qb] = need ? mt : m_run[qb];
+        l_part[qb][0] *= alpha;
+        l_part[qb][1] *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= alpha;
         }
-      }
-      // row max: in-lane over the 32 scores as a tree of three-way maxima (depth 4), then
-      // across the lane halves
-      float m1[11];
+        const float mneg = -m_run[qb];
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        m1[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
-        m1[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
-      }
-      m1[10] = fmaxf(s0[15], s1[15]);
-      const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
-      const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
-      float mx = fmaxf(fmaxf(fmaxf(m2a, m2b), m2c), m2d);
-      mx = xhalf_max(mx);
-      // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
-      const float mt = mx * c;
-      const bool need = mt > m_run + kThr;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-      m_run = need ? mt : m_run;
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int i = 0; i < Cfg::DB; ++i) oacc[i] *= alpha;
-      }
-      const float mneg = -m_run;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg)),
-                             (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[i + 1], c, mneg))};
-        const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg)),
-                             (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[i + 1], c, mneg))};
-        l_part[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(e0, ones, l_part[(i >> 1) & 1], false);
-        l_part[2 + ((i >> 1) & 1)] =
-            __builtin_amdgcn_fdot2_f32_bf16(e1, ones, l_part[2 + ((i >> 1) & 1)], false);
-        pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e0);
-        pw[2 + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, e1);
+          for (int h2 = 0; h2 < 2; ++h2) {  // key block 2t + h2
+            const f32x4_t &sv = s[2 * t + h2][qb];
+            const bf16x2_t e0 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(sv[0], c, mneg)),
+                                 (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[1], c, mneg))};
+            const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(sv[2], c, mneg)),
+                                 (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[3], c, mneg))};
+            l_part[qb][h2] = __builtin_amdgcn_fdot2_f32_bf16(e0, ones, l_part[qb][h2], false);
+            l_part[qb][h2] = __builtin_amdgcn_fdot2_f32_bf16(e1, ones, l_part[qb][h2], false);
+            pw[t][qb][2 * h2] = __builtin_bit_cast(uint32_t, e0);
+            pw[t][qb][2 * h2 + 1] = __builtin_bit_cast(uint32_t, e1);
+          }
+        }
       }
     }
     next(cc, 0);
@@ -708,14 +755,15 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // phase after the barrier, in the next.
   auto pin_softmax = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __asm__ volatile("" : "+v"(pw[i]));
-    __asm__ volatile("" : "+v"(l_part[0]), "+v"(l_part[1]), "+v"(l_part[2]), "+v"(l_part[3]),
-                     "+v"(m_run));
+    for (int t = 0; t < 2; ++t) __asm__ volatile("" : "+v"(pw[t][0]), "+v"(pw[t][1]));
+    __asm__ volatile("" : "+v"(l_part[0][0]), "+v"(l_part[0][1]), "+v"(l_part[1][0]),
+                     "+v"(l_part[1][1]), "+v"(m_run[0]), "+v"(m_run[1]));
   };
   auto pin_matrix = [&]() {
-    __asm__ volatile("" : "+v"(s0), "+v"(s1));
 #pragma unroll
-    for (int i = 0; i < Cfg::DB; ++i) __asm__ volatile("" : "+v"(oacc[i]));
+    for (int kb = 0; kb < 4; ++kb) __asm__ volatile("" : "+v"(s[kb][0]), "+v"(s[kb][1]));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) __asm__ volatile("" : "+v"(oacc[cb][0]), "+v"(oacc[cb][1]));
   };
   // Neither barrier may have arithmetic moved across it (the machine scheduler would otherwise
   // pull the exp work of a softmax phase into the neighbouring matrix phase).
@@ -783,7 +831,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
       {
         const lds_char *K0 = (const lds_char *)kbuf0;
 #pragma unroll
-        for (int ds = 0; ds < Cfg::DS; ++ds) qk_step(K0, ds);
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) qk_step(K0, kb, ks);
       }
       if (grp_a) {
         softmax_phase(cc);
@@ -820,29 +870,30 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     }
   }
 
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
-  const float l_tot = xhalf_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-  if (!qvalid) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.  A query's row sum is spread over
+  // its four lanes; lane l16 + 16*g4 stores channels cb*16 + 4*g4 .. +3 of its query.
   const Seg os = a.o[tile.q_kind];
-  __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh;
+  float *lse = a.lse[tile.q_kind];
 #pragma unroll
-  for (int db = 0; db < Cfg::DB; ++db) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = x16_sum(xhalf_sum(l_part[qb][0] + l_part[qb][1]));
+    if (!qvalid[qb]) continue;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow[qb] * os.sn + h * os.sh;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int cb = 0; cb < CB; ++cb) {
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
       bf16x4_t v;
-      v[0] = (__bf16)(oacc[db][g * 4 + 0] * inv);
-      v[1] = (__bf16)(oacc[db][g * 4 + 1] * inv);
-      v[2] = (__bf16)(oacc[db][g * 4 + 2] * inv);
-      v[3] = (__bf16)(oacc[db][g * 4 + 3] * inv);
-      *(bf16x4_t *)(op + db * 32 + g * 8 + 4 * hl) = v;
+      v[0] = (__bf16)(oacc[cb][qb][0] * inv);
+      v[1] = (__bf16)(oacc[cb][qb][1] * inv);
+      v[2] = (__bf16)(oacc[cb][qb][2] * inv);
+      v[3] = (__bf16)(oacc[cb][qb][3] * inv);
+      *(bf16x4_t *)(op + cb * 16 + 4 * g4) = v;
     }
+    if (lse && g4 == 0)
+      lse[(int64_t)w.bh * a.q_rows[tile.q_kind] + qrow[qb]] =
+          l_tot > 0.0f ? (m_run[qb] + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
   }
-  float *lse = a.lse[tile.q_kind];
-  if (lse && hl == 0)
-    lse[(int64_t)w.bh * a.q_rows[tile.q_kind] + qrow] =
-        l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
 }
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int block_m, int grid,
