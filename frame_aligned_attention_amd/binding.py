@@ -194,10 +194,12 @@ class Layout:
     def __init__(self, handle, owned=True):
         self.handle = handle
         self.owned = owned
+        self._lib = lib  # kept on the object: module globals may already be gone at exit
 
     def __del__(self):
-        if getattr(self, "owned", False) and self.handle:
-            lib.fa_layout_destroy(self.handle)
+        _lib = getattr(self, "_lib", None)
+        if getattr(self, "owned", False) and self.handle and _lib is not None:
+            _lib.fa_layout_destroy(self.handle)
             self.handle = None
 
 
@@ -262,10 +264,12 @@ class Stream:
         _check(lib.fa_stream_create(C.byref(desc), C.byref(h)), "fa_stream_create")
         self.handle = h
         self.desc = desc
+        self._lib = lib  # kept on the object: module globals may already be gone at exit
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            lib.fa_stream_destroy(self.handle)
+        _lib = getattr(self, "_lib", None)
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.fa_stream_destroy(self.handle)
             self.handle = None
 
     def chunk(self, io: fa_io, stream=None):

@@ -307,8 +307,9 @@ struct fa_stream {
   fa_layout_desc d;
   int32_t next_frame = 0;
   int32_t ring_first = 0;
-  std::vector<fa_layout *> cache;  // distinct block maps seen so far
-  fa_layout *current = nullptr;    // layout of the next chunk
+  std::vector<fa_layout *> cache;    // distinct block maps of the current reference set
+  std::vector<fa_layout *> retired;  // layouts handed out earlier, kept until destroy
+  fa_layout *current = nullptr;      // layout of the next chunk
 };
 
 namespace fa {
@@ -347,8 +348,8 @@ static fa_status stream_layout(fa_stream *s, fa_layout **out) {
       *out = c;
       return FA_OK;
     }
-  if (s->cache.size() >= 64) {
-    fa_layout_destroy(s->cache.front());
+  if (s->cache.size() >= 64) {  // stop matching against the oldest one; it stays valid
+    s->retired.push_back(s->cache.front());
     s->cache.erase(s->cache.begin());
   }
   s->cache.push_back(L);
@@ -357,9 +358,19 @@ static fa_status stream_layout(fa_stream *s, fa_layout **out) {
   return FA_OK;
 }
 
+// A layout the stream has handed out (fa_stream_layout, or a chunk still running on the device)
+// must stay valid until fa_stream_destroy: a new reference set only retires the cached ones.
 static void stream_reset_cache(fa_stream *s) {
-  for (fa_layout *c : s->cache) fa_layout_destroy(c);
+  s->retired.insert(s->retired.end(), s->cache.begin(), s->cache.end());
   s->cache.clear();
+  s->current = nullptr;
+}
+
+static void stream_free_layouts(fa_stream *s) {
+  for (fa_layout *c : s->cache) fa_layout_destroy(c);
+  for (fa_layout *c : s->retired) fa_layout_destroy(c);
+  s->cache.clear();
+  s->retired.clear();
   s->current = nullptr;
 }
 
@@ -457,7 +468,7 @@ extern "C" fa_status fa_stream_set_refs(fa_stream *s, int32_t n_ref, const int32
 
 extern "C" fa_status fa_stream_destroy(fa_stream *s) {
   if (!s) return FA_OK;
-  stream_reset_cache(s);
+  stream_free_layouts(s);
   delete s;
   return FA_OK;
 }

@@ -336,7 +336,11 @@ fa_status fa_stream_chunk(fa_stream *s, const fa_io *io, fa_hip_stream stream);
  * at the next frame position and advances the stream by d->frames.  Low-bit
  * streams call fa_stream_layout, fa_quantize_lowbit and fa_attn_fwd first. */
 fa_status fa_stream_advance(fa_stream *s, const fa_io *io, fa_hip_stream stream);
-/* The layout the next chunk will use (owned by the stream; valid until destroy). */
+/* The layout the next chunk will use.  Owned by the stream: every layout the stream hands
+ * out (here or inside fa_stream_chunk) stays valid, with its device block map, until
+ * fa_stream_destroy -- a new reference set (fa_stream_set_refs) only stops reusing the old
+ * ones -- so a HIP graph captured with it stays replayable for the stream's lifetime.  Work
+ * using a stream's layouts must complete before fa_stream_destroy. */
 fa_status fa_stream_layout(fa_stream *s, const fa_layout **out);
 /* next_frame: chunk_start of the next chunk; ring_first_frame: the ring holds
  * [ring_first_frame, next_frame) and the sink frames (== next_frame when it

@@ -1,9 +1,9 @@
 """HIP path (libfa.so through the C ABI) against the CPU oracle, element by
 element on the same seeded inputs.  Tolerances on O: fp32 max|d| <= 1e-5;
-bf16 max|d| <= 1e-2 and mean|d| <= 1e-3; plus LSE bounds (1e-4 fp32, 2e-3
-bf16) because under N(0,1) inputs |O| is ~0.01 and an O bound alone would
-not catch a wrong mask."""
-import math
+bf16 max|d| <= 1e-2 and mean|d| <= 1e-3; plus LSE bounds (1e-4 fp32; bf16 per
+row by its visible-key count, gpu_helpers.lse_tol_bf16) because under N(0,1)
+inputs |O| is ~0.01 and an O bound alone would not catch a wrong mask.  The
+Q = 0 closed forms at full size are in test_gpu_closed_form.py."""
 
 import numpy as np
 import pytest
@@ -12,7 +12,6 @@ import torch
 import fa_workloads as W
 import gpu_helpers as G
 from frame_aligned_attention_amd import binding as B
-from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 TGT, SRC, REF = G.TGT, G.SRC, G.REF
@@ -107,34 +106,6 @@ def test_bidirectional_full_size_sampled():
     c = workload_call(1)
     res = G.run_call(c)
     G.compare_sampled(c, res, n_rows=48, heads=[0, 7, 11], what="bidir full")
-
-
-def test_bidirectional_full_size_q_zero_closed_form():
-    """Q = 0: O is the mean of the visible V rows and LSE = ln(#visible) at full size."""
-    G.say("case: bidirectional bf16 full size, Q = 0 closed form")
-    c = workload_call(1)
-    for k in c.q:
-        c.q[k] = np.zeros_like(c.q[k])
-    res = G.run_call(c)
-    T, C = c.T, c.C
-    vt, vs, vr = (c.v_hist.astype(np.float64), c.v_src.astype(np.float64),
-                  c.v_ref.astype(np.float64))
-    sum_t, sum_r = vt.sum(0), vr.sum(0)
-    for f in (0, 1, 10, 20):
-        n_t = C * T + T + sum(c.ref_tokens)
-        mean_t = (sum_t + vs[f * T:(f + 1) * T].sum(0) + sum_r) / n_t
-        o, lse = res[TGT]
-        rows = [f * T, f * T + 777, f * T + T - 1]
-        G.tol_check(o[rows], np.broadcast_to(mean_t, (3,) + mean_t.shape), "bf16",
-                    "Q=0 target frame %d" % f, lse[:, rows], np.full((c.H, 3), math.log(n_t)))
-        n_s = T + sum(c.ref_tokens)
-        mean_s = (vs[f * T:(f + 1) * T].sum(0) + sum_r) / n_s
-        o, lse = res[SRC]
-        G.tol_check(o[rows], np.broadcast_to(mean_s, (3,) + mean_s.shape), "bf16",
-                    "Q=0 source frame %d" % f, lse[:, rows], np.full((c.H, 3), math.log(n_s)))
-    o, lse = res[REF]
-    G.tol_check(o[[0, 1559]], np.broadcast_to(sum_r / 1560, (2,) + sum_r.shape), "bf16",
-                "Q=0 reference rows", lse[:, [0, 1559]], np.full((c.H, 2), math.log(1560)))
 
 
 def stream_call(wid, cs, H=None) -> G.Call:
