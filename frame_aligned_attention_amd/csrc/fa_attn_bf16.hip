@@ -656,16 +656,19 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) pv_step(Vl, t, cb);
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read: K operands of pairs 0..2
+    // operands seven MFMA pairs ahead (~220 cycles of matrix work, the LDS latency under this
+    // load): K reads (one per QK pair), then V reads (two per PV pair).  Three pairs ahead was
+    // 2-3% slower.
+    constexpr int LA = 7;
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS read: K operands of pairs 0..LA-1
 #pragma unroll
     for (int i = 0; i < NQK + NPV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA pair (QK, then PV)
       if constexpr (decltype(with_loads)::value)
         if (i % EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-      // operands three MFMA pairs ahead: K reads (one per QK pair), then V reads (two per PV pair)
-      if (i + 3 < NQK)
+      if (i + LA < NQK)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      else if (i + 3 < NQK + NPV)
+      else if (i + LA < NQK + NPV)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
