@@ -89,6 +89,7 @@ def _load():
         "fa_layout_destroy": ([P], C.c_int),
         "fa_layout_prepare": ([P], C.c_int),
         "fa_attn_fwd": ([P, C.POINTER(fa_io), P], C.c_int),
+        "fa_attn_fwd_noalloc": ([P, C.POINTER(fa_io), P], C.c_int),
         "fa_quantize_lowbit": ([P, C.POINTER(fa_io), C.POINTER(fa_io), C.c_int32, P], C.c_int),
         "fa_ring_append": ([C.POINTER(fa_layout_desc)] + [C.POINTER(fa_tensor)] * 4 +
                            [C.c_int32, C.c_int32, P], C.c_int),
@@ -242,6 +243,11 @@ def fa_layout_prepare(L: Layout):
 
 def fa_attn_fwd(L: Layout, io: fa_io, stream=None):
     _check(lib.fa_attn_fwd(L.handle, C.byref(io), _stream_handle(stream)), "fa_attn_fwd")
+
+
+def fa_attn_fwd_noalloc(L: Layout, io: fa_io, stream=None):
+    _check(lib.fa_attn_fwd_noalloc(L.handle, C.byref(io), _stream_handle(stream)),
+           "fa_attn_fwd_noalloc")
 
 
 def fa_quantize_lowbit(L: Layout, io_in: fa_io, io_out: fa_io, flags: int = 0, stream=None):

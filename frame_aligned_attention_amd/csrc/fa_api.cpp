@@ -55,7 +55,8 @@ static const char *kOName[3] = {"o_tgt", "o_src", "o_ref"};
 static const char *kKName[4] = {"k_ring", "k_tgt", "k_src", "k_ref"};
 static const char *kVName[4] = {"v_ring", "v_tgt", "v_src", "v_ref"};
 
-static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t stream) {
+fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
+                       const DeviceMap *map) {
   if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
   if (!io) return fail(FA_ERR_INVALID, "io is NULL");
   const fa_layout_desc &d = L->d;
@@ -106,15 +107,19 @@ static fa_status attn_fwd(const fa_layout *L, const fa_io *io, hipStream_t strea
   a.scale = d.scale;
   a.c = d.scale * 1.4426950408889634f;
   if (L->work.empty()) return FA_OK;
-  // Under stream capture the block map must already be on the device (fa_layout_prepare).
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
-    (void)hipGetLastError();
-    capture = hipStreamCaptureStatusNone;
-  }
   DeviceMap m;
-  fa_status st = device_map(L, &m, capture == hipStreamCaptureStatusNone);
-  if (st != FA_OK) return st;
+  if (map) {
+    m = *map;
+  } else {
+    // Under stream capture the block map must already be on the device (fa_layout_prepare).
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+      (void)hipGetLastError();
+      capture = hipStreamCaptureStatusNone;
+    }
+    fa_status st = device_map(L, &m, capture == hipStreamCaptureStatusNone);
+    if (st != FA_OK) return st;
+  }
   a.tiles = m.tiles;
   a.ranges = m.ranges;
   a.work = m.work;
@@ -290,7 +295,7 @@ extern "C" const char *fa_status_str(fa_status s) {
 extern "C" const char *fa_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream) {
-  return attn_fwd(L, io, (hipStream_t)stream);
+  return attn_fwd_map(L, io, (hipStream_t)stream, nullptr);
 }
 
 extern "C" fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring,
@@ -424,7 +429,7 @@ extern "C" fa_status fa_stream_chunk(fa_stream *s, const fa_io *io, fa_hip_strea
   fa_layout *L = nullptr;
   fa_status st = stream_layout(s, &L);
   if (st != FA_OK) return st;
-  st = attn_fwd(L, io, (hipStream_t)stream);
+  st = attn_fwd_map(L, io, (hipStream_t)stream, nullptr);
   if (st != FA_OK) return st;
   return fa_stream_advance(s, io, stream);
 }

@@ -318,11 +318,44 @@ fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload) {
 
 using namespace fa;
 
+namespace fa {
+size_t map_image_bytes(const fa_layout *L, size_t *off_ranges, size_t *off_work) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t r = up(L->tiles.size() * sizeof(DevTile));
+  const size_t w = r + up(L->ranges.size() * sizeof(DevRange));
+  if (off_ranges) *off_ranges = r;
+  if (off_work) *off_work = w;
+  return w + up(L->work.size() * sizeof(DevWork));
+}
+}  // namespace fa
+
 extern "C" fa_status fa_layout_prepare(const fa_layout *L) {
   if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
   if (L->work.empty()) return FA_OK;
   DeviceMap m;
-  return device_map(L, &m, true);
+  fa_status st = device_map(L, &m, true);
+  if (st != FA_OK) return st;
+  // pinned host image of the block map, the source of fa_attn_fwd_noalloc's per-call copy
+  std::lock_guard<std::mutex> g(L->mu);
+  if (!L->pinned) {
+    size_t orr = 0, ow = 0;
+    const size_t bytes = map_image_bytes(L, &orr, &ow);
+    char *p = nullptr;
+    if (hipHostMalloc((void **)&p, bytes, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FA_ERR_NOMEM, "pinned host allocation of the block map image failed");
+    }
+    std::memset(p, 0, bytes);
+    std::memcpy(p, L->tiles.data(), L->tiles.size() * sizeof(DevTile));
+    std::memcpy(p + orr, L->ranges.data(), L->ranges.size() * sizeof(DevRange));
+    std::memcpy(p + ow, L->work.data(), L->work.size() * sizeof(DevWork));
+    fa_layout *M = const_cast<fa_layout *>(L);
+    M->off_ranges = orr;
+    M->off_work = ow;
+    L->pinned_bytes = bytes;
+    L->pinned = p;
+  }
+  return FA_OK;
 }
 
 extern "C" fa_status fa_layout_build(const fa_layout_desc *d, int32_t ring_first_frame,
@@ -393,6 +426,7 @@ extern "C" fa_status fa_layout_destroy(fa_layout *L) {
       }
       (void)hipSetDevice(cur);
     }
+    if (L->pinned) (void)hipHostFree(L->pinned);
   }
   delete L;
   return FA_OK;

@@ -35,6 +35,11 @@ struct fa_layout {
   double useful_pairs = 0, visited_pairs = 0, bytes = 0;
   mutable std::mutex mu;
   mutable std::map<int, fa::DeviceMap> dev;  // per HIP device id
+  // The block map as one pinned host image (tiles | ranges | work, each part 256-byte aligned),
+  // made by fa_layout_prepare; fa_attn_fwd_noalloc copies it into its static device array.
+  mutable char *pinned = nullptr;
+  mutable size_t pinned_bytes = 0;
+  size_t off_ranges = 0, off_work = 0;
 };
 
 namespace fa {
@@ -42,4 +47,10 @@ namespace fa {
 // The layout's block map on the current device.  Uploads it on first use unless may_upload is
 // false (a stream being captured into a graph must not allocate or copy synchronously).
 fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload = true);
+// Byte size of the block map as one image with each part 256-byte aligned (sets the offsets).
+size_t map_image_bytes(const fa_layout *L, size_t *off_ranges, size_t *off_work);
+// Checks the tensors of `io` against L and launches the attention kernel with the block map
+// `map` (or, if NULL, the layout's own device copy, uploaded on first use).
+fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
+                       const DeviceMap *map);
 }  // namespace fa

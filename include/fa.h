@@ -216,6 +216,22 @@ fa_status fa_layout_destroy(fa_layout *L);
 fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
 
 /*
+ * fa_attn_fwd for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same operation, outputs and checks as
+ * fa_attn_fwd, but the layout's block map is copied on every call (one host-to-device copy on
+ * `stream`, from the pinned image fa_layout_prepare makes) into a static device array of 4 MiB
+ * that the library holds on each GPU until the process ends, and the kernels read it there.
+ * The call allocates and frees nothing.  L must have been prepared on this device
+ * (fa_layout_prepare), else FA_ERR_INVALID.  A block map larger than the array (more than
+ * 4 MiB: tiles, ranges and the work list, each part rounded up to 256 bytes) returns
+ * FA_ERR_CAPACITY before anything is enqueued.  Every call on a GPU shares that GPU's array,
+ * which keeps the last call's map: calls ordered on one stream are safe, calls on different
+ * streams of one GPU that may overlap race (one call's copy can overwrite the map another
+ * call's kernel is reading).
+ */
+fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
+
+/*
  * Low-bit prologue for an FA_LOWBIT layout.  From the bf16 tensors of `in`:
  *  - a per-(batch, head) channel mean m of all keys the call reads (ring
  *    frames in view, chunk, source, references) into out->k_mean, or, with
