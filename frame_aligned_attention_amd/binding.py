@@ -22,7 +22,7 @@ FA_WINDOW_ALL = -1
 FA_MAX_REF = 8
 FA_SEG_RING, FA_SEG_TGT, FA_SEG_SRC, FA_SEG_REF = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_SAME_FRAME, FA_MASK_GATE = 0, 1, 2
-FA_QUANT_MEAN_GIVEN = 1
+FA_QUANT_MEAN_GIVEN, FA_QUANT_RING_READY = 1, 2
 
 
 class fa_layout_desc(C.Structure):
@@ -93,6 +93,8 @@ def _load():
         "fa_quantize_lowbit": ([P, C.POINTER(fa_io), C.POINTER(fa_io), C.c_int32, P], C.c_int),
         "fa_ring_append": ([C.POINTER(fa_layout_desc)] + [C.POINTER(fa_tensor)] * 4 +
                            [C.c_int32, C.c_int32, P], C.c_int),
+        "fa_ring_quantize": ([C.POINTER(fa_layout_desc)] + [C.POINTER(fa_tensor)] * 4 +
+                             [P, C.c_int32, C.c_int32, P], C.c_int),
         "fa_stream_create": ([C.POINTER(fa_layout_desc), C.POINTER(P)], C.c_int),
         "fa_stream_chunk": ([P, C.POINTER(fa_io), P], C.c_int),
         "fa_stream_advance": ([P, C.POINTER(fa_io), P], C.c_int),
@@ -260,6 +262,13 @@ def fa_ring_append(desc: fa_layout_desc, k_ring, v_ring, k_chunk, v_chunk, first
     ts = [tensor(x) for x in (k_ring, v_ring, k_chunk, v_chunk)]
     _check(lib.fa_ring_append(C.byref(desc), *[C.byref(t) for t in ts], first_frame, frames,
                               _stream_handle(stream)), "fa_ring_append")
+
+
+def fa_ring_quantize(desc: fa_layout_desc, k_ring, v_ring, k_codes, v_codes, k_scales, v_scales,
+                     k_mean, first_frame: int, frames: int, stream=None):
+    ts = [tensor(k_ring), tensor(v_ring), tensor(k_codes, k_scales), tensor(v_codes, v_scales)]
+    _check(lib.fa_ring_quantize(C.byref(desc), *[C.byref(t) for t in ts], _ptr(k_mean),
+                                first_frame, frames, _stream_handle(stream)), "fa_ring_quantize")
 
 
 class Stream:

@@ -191,7 +191,12 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
   if (!L || !in || !out) return fail(FA_ERR_INVALID, "NULL argument");
   const fa_layout_desc &d = L->d;
   if (d.dtype != FA_LOWBIT) return fail(FA_ERR_INVALID, "layout is not FA_LOWBIT");
-  if (flags & ~FA_QUANT_MEAN_GIVEN) return fail(FA_ERR_INVALID, "unknown flags");
+  if (flags & ~(FA_QUANT_MEAN_GIVEN | FA_QUANT_RING_READY))
+    return fail(FA_ERR_INVALID, "unknown flags");
+  const bool ring_ready = (flags & FA_QUANT_RING_READY) != 0;
+  if (ring_ready && !(flags & FA_QUANT_MEAN_GIVEN))
+    return fail(FA_ERR_INVALID, "FA_QUANT_RING_READY needs FA_QUANT_MEAN_GIVEN (the ring's key "
+                                "codes were made with that mean)");
   if (!out->k_mean || !out->v_absmax) return fail(FA_ERR_INVALID, "k_mean / v_absmax is NULL");
   const int T = d.tokens_per_frame;
   QuantArgs qa{};
@@ -217,9 +222,11 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
     g.kind = kind;
     g.lo0 = lo0; g.hi0 = hi0; g.lo1 = lo1; g.hi1 = hi1;
     g.blk_begin = blocks;
+    g.blk0 = 0;
+    g.nproc = g.nblk;
     g.n = ntok;
     g.lse = nullptr;
-    blocks += g.nblk;
+    blocks += g.nproc;
     return FA_OK;
   };
   const fa_tensor *qi[3] = {&in->q_tgt, &in->q_src, &in->q_ref};
@@ -256,6 +263,28 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
     for (int sgi = 0; sgi < 4; ++sgi) {
       if (!used[sgi]) continue;
       const int n = seg_tok[sgi];
+      if (sgi == FA_SEG_RING && ring_ready) {
+        // the ring's codes are kept by fa_ring_quantize; the V scales of the blocks in view
+        // still count towards v_absmax
+        if (kind == 1) continue;
+        const fa_tensor &vc = *vo[sgi];
+        if (!vc.scale) return fail(FA_ERR_INVALID, "v_ring: low-bit scale array is NULL");
+        for (int i = 0; i < nrun; ++i) {
+          if (rhi[i] <= rlo[i]) continue;
+          if (nseg >= kMaxQSeg) return fail(FA_ERR_UNSUPPORTED, "too many tensors to quantise");
+          QSeg &g = qa.seg[nseg++];
+          g = QSeg{};
+          g.scale = vc.scale;
+          g.nblk = (n + kQuantBlock - 1) / kQuantBlock;
+          g.kind = 3;
+          g.blk_begin = blocks;
+          g.blk0 = rlo[i] / kQuantBlock;
+          g.nproc = (rhi[i] - 1) / kQuantBlock - g.blk0 + 1;
+          g.n = n;
+          blocks += g.nproc;
+        }
+        continue;
+      }
       const int lo0 = sgi == FA_SEG_RING ? rlo[0] : 0, hi0 = sgi == FA_SEG_RING ? rhi[0] : n;
       const int lo1 = sgi == FA_SEG_RING ? rlo[1] : 0, hi1 = sgi == FA_SEG_RING ? rhi[1] : 0;
       st = add(kind == 1 ? *ki[sgi] : *vi[sgi], kind == 1 ? *ko[sgi] : *vo[sgi], n, kind, lo0,
@@ -271,9 +300,100 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
   return FA_OK;
 }
 
+// Re-quantises every 128-token block of the ring's code tensors that holds a token of frames
+// [first_frame, first_frame + frames), from the bf16 ring (whole blocks, so a block shared with a
+// neighbouring slot is coded from that slot's current bf16 contents too).
+static fa_status ring_quantize(const fa_layout_desc *d, const fa_tensor *k_ring,
+                               const fa_tensor *v_ring, const fa_tensor *k_codes,
+                               const fa_tensor *v_codes, const float *k_mean, int32_t first_frame,
+                               int32_t frames, hipStream_t stream) {
+  if (!d || !k_ring || !v_ring || !k_codes || !v_codes || !k_mean)
+    return fail(FA_ERR_INVALID, "NULL argument");
+  if (d->dtype != FA_LOWBIT) return fail(FA_ERR_INVALID, "descriptor is not FA_LOWBIT");
+  if (d->head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "low-bit head_dim must be 128");
+  if (d->cache_frames < 1 || d->tokens_per_frame < 1 || d->heads < 1 || d->batch < 1)
+    return fail(FA_ERR_INVALID, "bad geometry");
+  if (d->sink_frames < 0 || d->sink_frames > d->cache_frames)
+    return fail(FA_ERR_INVALID, "sink_frames must be in [0, cache_frames]");
+  if (first_frame < 0 || frames < 0) return fail(FA_ERR_INVALID, "negative frame range");
+  const int64_t nonsink =
+      (int64_t)first_frame + frames - std::max<int64_t>(first_frame, d->sink_frames);
+  if (nonsink > (int64_t)d->cache_frames - d->sink_frames)
+    return fail(FA_ERR_INVALID, "more non-sink frames than the ring's cycling slots");
+  if (frames == 0) return FA_OK;
+  const int T = d->tokens_per_frame;
+  const int ntok = d->cache_frames * T;
+  if ((int64_t)ntok * d->heads * d->batch >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "ring too large");
+  for (const fa_tensor *t : {k_ring, v_ring}) {
+    fa_status st = check_tensor(*t, 2, d->batch, t == k_ring ? "k_ring" : "v_ring", false);
+    if (st != FA_OK) return st;
+  }
+  for (const fa_tensor *t : {k_codes, v_codes}) {
+    fa_status st = check_tensor(*t, 1, d->batch, t == k_codes ? "k_codes" : "v_codes", true);
+    if (st != FA_OK) return st;
+  }
+  // block ranges touched by the frames' slots, merged
+  std::vector<std::pair<int, int>> br;  // [b0, b1)
+  for (int32_t g = first_frame; g < first_frame + frames; ++g) {
+    const int slot = ring_slot(g, d->sink_frames, d->cache_frames);
+    const int b0 = slot * T / kQuantBlock, b1 = ((slot + 1) * T + kQuantBlock - 1) / kQuantBlock;
+    br.push_back({b0, b1});
+  }
+  std::sort(br.begin(), br.end());
+  std::vector<std::pair<int, int>> merged;
+  for (auto &r : br) {
+    if (!merged.empty() && r.first <= merged.back().second)
+      merged.back().second = std::max(merged.back().second, r.second);
+    else
+      merged.push_back(r);
+  }
+  QuantArgs qa{};
+  qa.H = d->heads;
+  qa.D = d->head_dim;
+  qa.batch = d->batch;
+  qa.k_mean = const_cast<float *>(k_mean);
+  qa.v_absmax = nullptr;
+  qa.softmax_scale = d->scale;
+  int nseg = 0, blocks = 0;
+  for (int kind = 1; kind <= 2; ++kind)
+    for (auto &r : merged) {
+      if (nseg >= kMaxQSeg) return fail(FA_ERR_UNSUPPORTED, "too many block runs in one call");
+      const fa_tensor &ti = kind == 1 ? *k_ring : *v_ring;
+      const fa_tensor &to = kind == 1 ? *k_codes : *v_codes;
+      QSeg &g = qa.seg[nseg++];
+      g = QSeg{};
+      g.in = ti.data; g.isb = ti.stride_b; g.isn = ti.stride_n; g.ish = ti.stride_h;
+      g.out = to.data; g.osb = to.stride_b; g.osn = to.stride_n; g.osh = to.stride_h;
+      g.scale = to.scale;
+      g.nblk = (ntok + kQuantBlock - 1) / kQuantBlock;
+      g.kind = kind;
+      g.lo0 = r.first * kQuantBlock;
+      g.hi0 = std::min(r.second * kQuantBlock, ntok);
+      g.blk_begin = blocks;
+      g.blk0 = r.first;
+      g.nproc = r.second - r.first;
+      g.n = ntok;
+      blocks += g.nproc;
+    }
+  qa.nseg = nseg;
+  qa.total_blocks = blocks;
+  hipError_t e = launch_quant_lowbit(qa, true, stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("ring quantiser: ") + hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace fa
 
 using namespace fa;
+
+extern "C" fa_status fa_ring_quantize(const fa_layout_desc *d, const fa_tensor *k_ring,
+                                      const fa_tensor *v_ring, const fa_tensor *k_codes,
+                                      const fa_tensor *v_codes, const float *k_mean,
+                                      int32_t first_frame, int32_t frames, fa_hip_stream stream) {
+  return ring_quantize(d, k_ring, v_ring, k_codes, v_codes, k_mean, first_frame, frames,
+                       (hipStream_t)stream);
+}
 
 extern "C" fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out,
                                         int32_t flags, fa_hip_stream stream) {

@@ -105,10 +105,12 @@ struct QSeg {
   void *out;
   int64_t osb, osn, osh;  // elements (bytes)
   float *scale;           // [batch][heads][nblk]
-  int32_t nblk;
-  int32_t kind;           // 0: Q int8, 1: K int8 after the mean, 2: V e4m3
+  int32_t nblk;           // blocks of the tensor (row length of `scale`)
+  int32_t kind;           // 0: Q int8, 1: K int8 after the mean, 2: V e4m3,
+                          // 3: V already coded -- only fold its block scales into v_absmax
   int32_t lo0, hi0, lo1, hi1;
   int32_t blk_begin;      // first entry of this tensor in the flat block list
+  int32_t blk0, nproc;    // the tensor's blocks blk0 .. blk0 + nproc - 1 are processed
   int32_t n;              // tokens
   float *lse;             // Q tensors: per-row smoothing shift scale*q.m -> [batch][heads][n]
 };
@@ -121,7 +123,7 @@ struct QuantArgs {
   int32_t total_blocks;   // sum of nblk
   int32_t H, D, batch;
   float *k_mean;          // [batch][heads][D]
-  float *v_absmax;        // [batch][heads]: largest V block scale, written with atomic max
+  float *v_absmax;        // [batch][heads]: largest V block scale (atomic max); NULL = not kept
   float softmax_scale;
 };
 

@@ -111,8 +111,14 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
   int si = 0;
   while (si + 1 < a.nseg && a.seg[si + 1].blk_begin <= flat) ++si;
   const QSeg &g = a.seg[si];
-  const int blk = flat - g.blk_begin;
+  const int blk = g.blk0 + (flat - g.blk_begin);
   const int t = threadIdx.x, lane16 = t & 15, rsub = t >> 4;
+  if (g.kind == 3) {  // codes made earlier: only their scale counts towards v_absmax
+    if (t == 0)
+      atomicMax((unsigned int *)(a.v_absmax + bh),
+                __float_as_uint(g.scale[(int64_t)bh * g.nblk + blk]));
+    return;
+  }
   const int c0 = lane16 * 8;
   const bool need_m = g.kind == 1 || (g.kind == 0 && g.lse);
   float m[8];
@@ -169,7 +175,8 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
   const float inv = amax > 0.0f ? qmax / amax : 0.0f;
   if (t == 0) {
     g.scale[(int64_t)bh * g.nblk + blk] = scale;
-    if (g.kind == 2) atomicMax((unsigned int *)(a.v_absmax + bh), __float_as_uint(scale));
+    if (g.kind == 2 && a.v_absmax)
+      atomicMax((unsigned int *)(a.v_absmax + bh), __float_as_uint(scale));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -202,7 +209,8 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
 
 hipError_t launch_quant_lowbit(const QuantArgs &a, bool mean_given, hipStream_t s) {
   const int nbh = a.batch * a.H;
-  hipLaunchKernelGGL(quant_init_kernel, dim3((nbh + 63) / 64), dim3(64), 0, s, a.v_absmax, nbh);
+  if (a.v_absmax)
+    hipLaunchKernelGGL(quant_init_kernel, dim3((nbh + 63) / 64), dim3(64), 0, s, a.v_absmax, nbh);
   if (!mean_given)
     hipLaunchKernelGGL(kmean_kernel, dim3(nbh * kMeanSplit), dim3(kMeanThreads), 0, s, a);
   if (a.total_blocks > 0)

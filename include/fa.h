@@ -250,8 +250,12 @@ fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream
  * quantiser writes that per-row shift there, and fa_attn_fwd on the low-bit
  * layout adds it to the LSE it computes.  Pass the same lse_* buffers to both
  * calls (or NULL to both).
+ * FA_QUANT_RING_READY (needs FA_QUANT_MEAN_GIVEN): the ring's codes and scales in
+ * out->k_ring / out->v_ring are kept up to date by fa_ring_quantize, with the same mean; the ring
+ * is then not read or quantised here, and only the scales of its V blocks in view are folded
+ * into v_absmax.  The per-call work is Q, the chunk, its source frames and the references.
  */
-enum { FA_QUANT_MEAN_GIVEN = 1 };
+enum { FA_QUANT_MEAN_GIVEN = 1, FA_QUANT_RING_READY = 2 };
 fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out, int32_t flags,
                              fa_hip_stream stream);
 
@@ -263,11 +267,30 @@ fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *o
  * sink_frames-1).  At most cache_frames - sink_frames non-sink frames per
  * call, else FA_ERR_INVALID.  Batch above 32767, or 2^31 or more (token, head)
  * rows in one append, return FA_ERR_UNSUPPORTED.  Element type from d->dtype
- * (FA_LOWBIT rings hold bf16 and are quantised per call).  Asynchronous.
+ * (FA_LOWBIT rings hold bf16; fa_ring_quantize keeps a coded copy).  Asynchronous.
  */
 fa_status fa_ring_append(const fa_layout_desc *d, const fa_tensor *k_ring, const fa_tensor *v_ring,
                          const fa_tensor *k_chunk, const fa_tensor *v_chunk, int32_t first_frame,
                          int32_t frames, fa_hip_stream stream);
+
+/*
+ * Low-bit ring kept coded at append time (the low-bit attention of the launch article's
+ * technical-stack section and the tech report's hybrid-attention paragraph, with the
+ * sliding-window KV cache of the structured summary's section 4.3): after fa_ring_append has
+ * put frames [first_frame, first_frame + frames) into the bf16 ring k_ring / v_ring, this
+ * re-quantises every 128-token block of the ring tensor that holds any of their tokens, from
+ * the bf16 ring, into k_codes (int8, keys minus k_mean [batch][heads][head_dim]) and v_codes
+ * (e4m3) -- the same layout as the ring with 1-byte elements, scales per (batch, head, block)
+ * in their .scale arrays, arithmetic as in fa_quantize_lowbit.  A block shared with a
+ * neighbouring slot is coded whole from that slot's current bf16 contents, so ring slots never
+ * written must hold finite values (zeros).  The codes then serve every later low-bit call with
+ * FA_QUANT_RING_READY and the same k_mean.  d: the stream's FA_LOWBIT descriptor (ring geometry,
+ * sink frames, heads, batch; head_dim 128).  Argument errors FA_ERR_INVALID before any launch;
+ * asynchronous.
+ */
+fa_status fa_ring_quantize(const fa_layout_desc *d, const fa_tensor *k_ring, const fa_tensor *v_ring,
+                           const fa_tensor *k_codes, const fa_tensor *v_codes, const float *k_mean,
+                           int32_t first_frame, int32_t frames, fa_hip_stream stream);
 
 /*
  * QK prologue: RMSNorm over head_dim then rotary position embedding over three

@@ -320,3 +320,121 @@ def test_lowbit_batch2_matches_single_calls(case):
             nm = G.KIND_NAMES[k]
             assert np.array_equal(G.host(out["o_" + nm])[b], o), (b, nm)
             assert np.array_equal(G.host(out["lse_" + nm])[b], lse), (b, nm)
+
+
+RING_Q_CASES = [
+    # seed, T, H, ring frames, sink frames, appended (first_frame, frames) in order
+    (80, 50, 2, 5, 0, [(0, 3), (3, 3)]),      # second append wraps: frames 3, 4, 5 -> slots 3, 4, 0
+    (81, 40, 3, 6, 2, [(0, 3), (3, 3), (6, 3)]),  # sink slots 0, 1; the others cycle through 2..5
+]
+
+
+@pytest.mark.parametrize("case", RING_Q_CASES, ids=["rq%d" % c[0] for c in RING_Q_CASES])
+def test_ring_quantize_codes_match_oracle(case):
+    """fa_ring_quantize after each fa_ring_append: every 128-token block of the ring that holds
+    an appended token has the oracle quantiser's codes and scales for that block's current bf16
+    contents (keys less the given mean); every other block keeps what it held."""
+    seed, T, H, cap, sink, appends = case
+    G.say("case: ring quantiser %s" % (case,))
+    g = np.random.default_rng(seed)
+    d = B.make_desc(3, T, H, 128, cache_frames=cap, sink_frames=sink, dtype=B.FA_LOWBIT)
+    n = cap * T
+    ring = {k: torch.zeros((1, n, H, 128), dtype=torch.bfloat16, device="cuda")
+            for k in ("k", "v")}
+    codes = {"k": torch.full((1, n, H, 128), 99, dtype=torch.int8, device="cuda"),
+             "v": torch.full((1, n, H, 128), 99, dtype=torch.uint8, device="cuda")}
+    scales = {k: torch.full((1, H, nblk(n)), -1.0, dtype=torch.float32, device="cuda")
+              for k in ("k", "v")}
+    mean = (g.standard_normal((H, 128)) * 2).astype(np.float32)
+    k_mean = torch.from_numpy(mean).reshape(1, H, 128).cuda()
+    for f0, nf in appends:
+        before = {k: (codes[k].clone(), scales[k].clone()) for k in codes}
+        kc = W.round_bf16(g.standard_normal((nf * T, H, 128)).astype(np.float32) * 2 +
+                          mean[None])
+        vc = W.round_bf16(g.standard_normal((nf * T, H, 128)).astype(np.float32))
+        B.fa_ring_append(d, ring["k"], ring["v"], G.dev(kc), G.dev(vc), f0, nf)
+        B.fa_ring_quantize(d, ring["k"], ring["v"], codes["k"], codes["v"], scales["k"],
+                           scales["v"], k_mean, f0, nf)
+        torch.cuda.synchronize()
+        touched = set()
+        for f in range(f0, f0 + nf):
+            s = G.ring_slot(f, sink, cap)
+            touched |= set(range(s * T // 128, ((s + 1) * T + 127) // 128))
+        kr, vr = G.host(ring["k"])[0], G.host(ring["v"])[0]
+        want = {"k": O.quant_int8(kr, mean=mean), "v": O.quant_e4m3(vr)}
+        for k in ("k", "v"):
+            got_c, got_s = codes[k].cpu().numpy()[0], scales[k].cpu().numpy()[0]
+            old_c, old_s = before[k][0].cpu().numpy()[0], before[k][1].cpu().numpy()[0]
+            for b in range(nblk(n)):
+                sl = slice(b * 128, min(n, (b + 1) * 128))
+                if b in touched:
+                    assert np.array_equal(got_s[:, b], want[k][1][:, b]), (k, b)
+                    assert np.array_equal(got_c[sl], want[k][0][sl].view(got_c.dtype)), (k, b)
+                else:
+                    assert np.array_equal(got_s[:, b], old_s[:, b]), (k, b, "scale moved")
+                    assert np.array_equal(got_c[sl], old_c[sl]), (k, b, "codes moved")
+
+
+def test_lowbit_stream_with_quantised_ring():
+    """Eight chunks of the low-bit workload (2 heads) with the ring kept coded at append time:
+    per chunk fa_quantize_lowbit with FA_QUANT_MEAN_GIVEN | FA_QUANT_RING_READY (Q, chunk,
+    source, reference only), fa_attn_fwd, fa_stream_advance (bf16 ring) and fa_ring_quantize
+    (coded ring), against the fp32 oracle on the unquantised inputs.  The key mean is fixed for
+    the stream: the oracle's mean of the reference and first-chunk keys."""
+    G.say("case: low-bit stream with a coded ring, 8 chunks, 2 heads")
+    w = W.WORKLOADS[4]
+    H = 2
+    d = B.make_desc(w.C, w.T, H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0, chunk_start=0,
+                    window=w.window, cache_frames=w.cache_frames, query_rows=1, dtype=B.FA_LOWBIT)
+    s = B.Stream(d)
+    n_ring = w.cache_frames * w.T
+    ring = {n: torch.zeros((1, n_ring, H, w.D), dtype=torch.bfloat16, device="cuda")
+            for n in ("k_ring", "v_ring")}
+    ring_codes = {"k_ring": torch.zeros((1, n_ring, H, w.D), dtype=torch.int8, device="cuda"),
+                  "v_ring": torch.zeros((1, n_ring, H, w.D), dtype=torch.uint8, device="cuda")}
+    ring_scales = {n: torch.zeros((1, H, nblk(n_ring)), dtype=torch.float32, device="cuda")
+                   for n in ring_codes}
+    r = W.ref_tensors(w, H=H)
+    mean = O.kmean([r["k_ref"], W.chunk_tensors(w, 0, H=H)["k_tgt"]])
+    k_mean = torch.from_numpy(mean).reshape(1, H, w.D).cuda()
+    ks, vs = [], []
+    for ch in range(8):
+        x = W.chunk_tensors(w, ch, H=H)
+        t = {"q_tgt": G.dev(x["q_tgt"]), "k_tgt": G.dev(x["k_tgt"]), "v_tgt": G.dev(x["v_tgt"]),
+             "k_src": G.dev(x["k_src"]), "v_src": G.dev(x["v_src"]),
+             "k_ref": G.dev(r["k_ref"]), "v_ref": G.dev(r["v_ref"]), **ring}
+        codes = {n: torch.empty(v.shape, dtype=torch.uint8 if n.startswith("v_") else torch.int8,
+                                device="cuda") for n, v in t.items() if n not in ring}
+        scales = {n: torch.empty((1, H, nblk(v.shape[1])), dtype=torch.float32, device="cuda")
+                  for n, v in t.items() if n not in ring}
+        codes.update(ring_codes)
+        scales.update(ring_scales)
+        rows = w.C * w.T
+        out = {"o_tgt": torch.empty((1, rows, H, w.D), dtype=torch.bfloat16, device="cuda"),
+               "lse_tgt": torch.empty((1, H, rows), dtype=torch.float32, device="cuda"),
+               "v_absmax": torch.empty((1, H), dtype=torch.float32, device="cuda")}
+        L = s.layout()
+        B.fa_quantize_lowbit(L, B.make_io(t), B.make_io({**codes, "lse_tgt": out["lse_tgt"],
+                                                         "k_mean": k_mean,
+                                                         "v_absmax": out["v_absmax"]}, scales),
+                             B.FA_QUANT_MEAN_GIVEN | B.FA_QUANT_RING_READY)
+        B.fa_attn_fwd(L, B.make_io({**codes, **out}, scales))
+        first = s.state()[0]
+        s.advance(B.make_io(t))
+        B.fa_ring_quantize(d, ring["k_ring"], ring["v_ring"], ring_codes["k_ring"],
+                           ring_codes["v_ring"], ring_scales["k_ring"], ring_scales["v_ring"],
+                           k_mean, first, w.C)
+        torch.cuda.synchronize()
+        ks.append(x["k_tgt"]); vs.append(x["v_tgt"])
+        cs = ch * w.C
+        lo = max(0, cs - w.window)
+        c = G.Call(T=w.T, C=w.C, H=H, D=w.D, dtype="lowbit", cs=cs, window=w.window,
+                   cache=w.cache_frames, ref_tokens=list(w.ref_tokens), ref_t0=list(w.ref_t0),
+                   query_rows=1, hist_first=lo)
+        c.k_hist = np.concatenate(ks[lo // w.C:])
+        c.v_hist = np.concatenate(vs[lo // w.C:])
+        c.q = {TGT: x["q_tgt"]}
+        c.k_src, c.v_src, c.k_ref, c.v_ref = x["k_src"], x["v_src"], r["k_ref"], r["v_ref"]
+        G.compare_sampled(c, {TGT: (G.host(out["o_tgt"])[0], G.host(out["lse_tgt"])[0])},
+                          n_rows=32, what="lowbit coded-ring chunk %d" % ch)
+    assert s.state() == (24, 12)
