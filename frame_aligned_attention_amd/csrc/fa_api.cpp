@@ -100,8 +100,6 @@ fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
     a.k[s] = seg_of(*ks[s], seg_tok[s]);
     a.v[s] = seg_of(*vs[s], seg_tok[s]);
   }
-  if (low && !io->v_absmax) return fail(FA_ERR_INVALID, "v_absmax is NULL");
-  a.v_absmax = io->v_absmax;
   a.T = T;
   a.H = d.heads;
   a.scale = d.scale;
@@ -197,7 +195,7 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
   if (ring_ready && !(flags & FA_QUANT_MEAN_GIVEN))
     return fail(FA_ERR_INVALID, "FA_QUANT_RING_READY needs FA_QUANT_MEAN_GIVEN (the ring's key "
                                 "codes were made with that mean)");
-  if (!out->k_mean || !out->v_absmax) return fail(FA_ERR_INVALID, "k_mean / v_absmax is NULL");
+  if (!out->k_mean) return fail(FA_ERR_INVALID, "k_mean is NULL");
   const int T = d.tokens_per_frame;
   QuantArgs qa{};
   qa.H = d.heads;
@@ -264,9 +262,9 @@ static fa_status quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_i
       if (!used[sgi]) continue;
       const int n = seg_tok[sgi];
       if (sgi == FA_SEG_RING && ring_ready) {
-        // the ring's codes are kept by fa_ring_quantize; the V scales of the blocks in view
-        // still count towards v_absmax
-        if (kind == 1) continue;
+        // the ring's codes are kept by fa_ring_quantize; only a requested v_absmax still takes
+        // the V scales of the blocks in view
+        if (kind == 1 || !out->v_absmax) continue;
         const fa_tensor &vc = *vo[sgi];
         if (!vc.scale) return fail(FA_ERR_INVALID, "v_ring: low-bit scale array is NULL");
         for (int i = 0; i < nrun; ++i) {

@@ -70,7 +70,6 @@ struct AttnArgs {
   const DevTile *tiles;
   const DevRange *ranges;
   const DevWork *work;
-  const float *v_absmax;  // low-bit: [b][h]
 };
 
 struct RingArgs {

@@ -9,14 +9,15 @@
 //    the softmax does not change (q.m is constant along a row);
 //  - Q and K: symmetric int8 per (batch, head, 128-token block), scale
 //    absmax/127, code = round_half_even(x * (127/absmax));
-//  - V: OCP e4m3 per block, scale absmax/448 (v_cvt_pk_fp8_f32 rounds to
-//    nearest even);
-//  - scores s = (q8 . k8) * sq * sk * softmax_scale, exact running max,
-//    p = 2^(s*log2e - m) in fp32, row sums l of p in fp32;
-//  - P.V in e4m3: p' = p * 448 * sv / U with U the largest V block scale of the
-//    call, so p' <= 448; O = (U / 448) * sum(p' v8) / l.  The kernel forms p'
-//    directly as 2^(s*log2e - m + log2(448 sv / U)) and adds sum(p') * U / (448 sv)
-//    to l once per tile.
+//  - V: OCP e4m3 per block with a power-of-two scale 2^e, the smallest with
+//    448 * 2^e >= absmax (so the largest code lies in (224, 448]), codes
+//    x * 2^-e rounded to nearest even by v_cvt_pk_fp8_f32;
+//  - scores s = (q8 . k8) * sq * sk * softmax_scale, online softmax in fp32
+//    with p = 2^(s*log2e - m);
+//  - P.V in e4m3: p' = p * 2^8 <= 256 (exact running max), and
+//    each tile's V block scale 2^e is applied by the MFMA's e8m0 scale of V;
+//    O = sum(2^e p' v8) / l with l = sum(p') taken by an MFMA on the same e4m3
+//    p' (numerator and denominator weigh every key alike).
 // Key tiles never straddle a 128-token block (a range's first tile ends at the
 // next 64-key boundary), so K and V scales are uniform per tile.
 #include "fa_device.h"
@@ -28,6 +29,7 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // ============================================================== quantiser
@@ -170,9 +172,19 @@ __global__ void __launch_bounds__(256) quant_kernel(const QuantArgs a) {
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float qmax = g.kind == 2 ? 448.0f : 127.0f;
-  const float scale = amax / qmax;
-  const float inv = amax > 0.0f ? qmax / amax : 0.0f;
+  float scale, inv;
+  if (g.kind == 2) {
+    // V: the smallest power of two 2^e (e >= -126) with 448 * 2^e >= amax.  For amax =
+    // 1.f * 2^(E - 127) that is e = E - 135, plus one when 1.f > 1.75; a subnormal amax takes
+    // the floor.  Codes x * 2^-e are exact scalings before the e4m3 rounding.
+    const uint32_t bits = __float_as_uint(amax);
+    const int e = max((int)(bits >> 23) - 135 + ((bits & 0x7fffffu) > 0x600000u ? 1 : 0), -126);
+    scale = amax > 0.0f ? __uint_as_float((uint32_t)(e + 127) << 23) : 0.0f;
+    inv = amax > 0.0f ? __uint_as_float((uint32_t)(127 - e) << 23) : 0.0f;
+  } else {
+    scale = amax / 127.0f;
+    inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  }
   if (t == 0) {
     g.scale[(int64_t)bh * g.nblk + blk] = scale;
     if (g.kind == 2 && a.v_absmax)
@@ -238,12 +250,27 @@ __device__ __forceinline__ int sw(int r) { return ((r >> 2) & 1) | (r & 2) | ((r
 
 // Work split as in the bf16 kernels: 4 waves of 32 query rows per 128-row work item, keys as the M
 // dimension.  Per 64-key tile: S^T = K Q^T on 8 int8 MFMAs, softmax, O^T += V^T P^T on 4 e4m3
-// MFMAs.  The loads of tile j+1 go out at the start of step j into the other LDS buffers; the
-// step itself runs S, softmax and PV of tile j in order.  With 1-byte tiles (32 KB of LDS per
-// workgroup) and 168 VGPRs, three workgroups share a CU, and the waves of the other two
-// workgroups fill each wave's dependency gaps.
-__global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
+// MFMAs and the row sums on one more.  The loads of tile j+1 go out at the start of step j into
+// the other LDS buffers; the step itself runs S, softmax and PV of tile j in order.  Two
+// workgroups share a CU (32 KB of LDS each); the waves of the other one fill each wave's
+// dependency gaps.
+//
+// The softmax is VALU-bound, so three things keep VALU work off it:
+//  - the int32 score accumulators start at the bits of the float kBias = 1.5 * 2^23: |q.k| <=
+//    128 * 127^2 < 2^22, so the sum's bits read as the float kBias + q.k exactly and no integer
+//    to float conversion is needed; kBias * fk is folded into the exp FMA (that term rounds
+//    once per tile, to under one unit of the integer score, far below the int8 rounding of q.k);
+//  - V block scales are powers of two, applied by the PV MFMA's own e8m0 block scale, so every
+//    tile takes p' = p * 2^(8 - kThr) with no per-tile weight;
+//  - the row sums of p' come from a 16x16x128 e4m3 MFMA of a ones pattern against P^T (the same
+//    e4m3 values the PV product uses), not from 32 adds.
+// The running max is exact (kThr = 0): a lazy one (p up to 4) cost accuracy on small rows.
+__global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
   using namespace lb;
+  constexpr int kBiasBits = 0x4B400000;
+  constexpr float kBias = 12582912.0f;
+  constexpr float kThr = 0.0f;
+  constexpr float kPShift = 8.0f - kThr;  // p' = p * 2^kPShift <= 256
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
@@ -272,9 +299,7 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   }
   // Q tiles are 128-row aligned: one Q block per workgroup
   const float sq = *((const cFloat *)qs.scale + (int64_t)w.bh * qs.nblk + tile.row0 / 128);
-  const float U = *((const cFloat *)a.v_absmax + w.bh);
   const float cq = sq * a.c;  // times sk gives the log2-domain scale of an int score
-  const float w448u = U > 0.0f ? 448.0f / U : 0.0f;  // times sv gives the V weight of a block
   const int fq = qrow / T;
 
   // ---- LDS read offsets
@@ -351,49 +376,62 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) load_one(rv, c.vsn, vbuf, j);
   };
-  // per-tile scales of the tile at cursor c: log2-domain score factor and the V weight
-  auto tile_scales = [&](const Cur &c, float &fk, float &wv) {
+  // per-tile scales of the tile at cursor c: log2-domain score factor, and the V block scale
+  // 2^e as its e8m0 code e + 127 (the float's exponent field; 0 for an all-zero block, whose
+  // codes are 0)
+  auto tile_scales = [&](const Cur &c, float &fk, int &ve8) {
     const Seg ks = a.k[c.seg], vs = a.v[c.seg];
     const int blk = c.k >> 7;
     const float sk = *((const cFloat *)ks.scale + (int64_t)w.bh * ks.nblk + blk);
     const float sv = *((const cFloat *)vs.scale + (int64_t)w.bh * vs.nblk + blk);
     fk = fmaxf(cq * sk, 1e-30f);  // an all-zero Q or K block: scores 0, masks stay -inf
-    wv = sv * w448u;
+    ve8 = (int)((__float_as_uint(sv) >> 23) & 0xffu);
   };
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
-  float l_part = 0.0f;
+  // finite start: the first tile with a visible key always raises it (a row with none keeps
+  // l = 0, its exp arguments all -inf)
+  float m_run = -1e30f;
+  // Row sums: D of v_mfma_scale_f32_16x16x128_f8f6f4 with A = a ones pattern and B = P^T.  Lane l
+  // of P^T holds query l % 32 (32 of its 64 keys; lane l + 32 the others), and a 16x16x128
+  // product pairs lane 16g + i of A with lane 16g + j of B over the same 32 bytes.  A row 0 of
+  // ones on the lanes of groups g = 0, 2 and a row 1 on groups 1, 3 make D[0][j] the sum of
+  // query j and D[1][j] that of query j + 16: lanes 0-15 hold them in lacc[0] and lacc[1].
+  f32x4_t lacc = f32x4_t{};
+  i32x8_t ones;
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int ov = i16 == (g16 & 1) ? 0x38383838 : 0;  // e4m3 1.0 = 0x38
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = ov;
+  }
+  i32x16_t sbias;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sbias[i] = kBiasBits;
 
   auto qk = [&](const char *kbuf, i32x16_t &s0, i32x16_t &s1) {
     const lds_char *Kl = (const lds_char *)kbuf;
-    s0 = i32x16_t{};
-    s1 = i32x16_t{};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       const i32x4_t a0 = *(const i32x4_t *)(Kl + (koff0 ^ (ds << 5)));
       const i32x4_t a1 = *(const i32x4_t *)(Kl + 32 * ROWB + (koff0 ^ (ds << 5)));
-      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[ds], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[ds], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[ds], ds == 0 ? sbias : s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[ds], ds == 0 ? sbias : s1, 0, 0, 0);
     }
   };
 
-  // softmax + PV of the tile at cursor c with integer scores (s0, s1) and V in `vbuf`
+  // softmax + PV of the tile at cursor c with scores (s0, s1) and V in `vbuf`
   auto softmax_pv = [&](const Cur &c, const i32x16_t &s0, const i32x16_t &s1, const char *vbuf) {
-    float fk, wv;
-    tile_scales(c, fk, wv);
-    // p' = p * wv is formed as 2^(s fk - m + log2 wv), and the row sum takes sum(p') / wv once
-    // per tile.  A zero weight (an all-zero V block) is raised to 2^-60: p' <= 2^-60 still codes
-    // to 0 in e4m3, and sum(p') * 2^60 still gives the row sum.
-    const float wvc = fmaxf(wv, 0x1p-60f);
-    const float lw = __builtin_amdgcn_logf(wvc), iw = __builtin_amdgcn_rcpf(wvc);
-    float x0[16], x1[16];
+    float fk;
+    int ve8;
+    tile_scales(c, fk, ve8);
+    float x0[16], x1[16];  // kBias + score, exactly
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      x0[i] = (float)s0[i];
-      x1[i] = (float)s1[i];
+      x0[i] = __builtin_bit_cast(float, (int)s0[i]);
+      x1[i] = __builtin_bit_cast(float, (int)s1[i]);
     }
     if (c.mask != FA_MASK_NONE || c.kend - c.k < BN) {
       int klo = c.begin, khi = c.kend;
@@ -418,18 +456,22 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x1[i]);
     mx = xhalf_max(mx);
-    const float mt = mx * fk;  // fk > 0
-    const bool need = mt > m_run;
+    const float mt = (mx - kBias) * fk;  // the difference is exact; fk > 0; -inf stays -inf
+    const bool need = mt > m_run + kThr;
     const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
     m_run = need ? mt : m_run;
-    l_part *= alpha;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+      // lanes 0-15 hold the sums of queries l and l + 16: the latter's alpha from lane l + 16
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha),
+                                                      false, false);
+      lacc[0] *= alpha;
+      lacc[1] *= __uint_as_float(r[1]);
     }
-    const float mneg = (m_run == -__builtin_inff() ? 0.0f : -m_run) + lw;
-    float lt = 0.0f;  // sum of p' over the tile
-    i32x8_t pw;       // P^T: byte kb*16 + r of the lane's 32 keys
+    // exp2 argument s fk - m + kPShift, with s fk = (kBias + s) fk - kBias fk
+    const float mneg = (kPShift - m_run) - kBias * fk;
+    i32x8_t pw;  // P^T: byte kb*16 + r of the lane's 32 keys
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
       float e[8];
@@ -438,8 +480,6 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
         e[j] = __builtin_amdgcn_exp2f(fmaf(x0[i + j], fk, mneg));
         e[4 + j] = __builtin_amdgcn_exp2f(fmaf(x1[i + j], fk, mneg));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lt += e[j];
       // each packing writes one half of its word and keeps the other: the first of a pair is
       // seeded with a dead register instead of a zero
       const int o0 = __builtin_bit_cast(int, e[0]), o1 = __builtin_bit_cast(int, e[4]);
@@ -448,7 +488,6 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
       v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4], e[5], o1, false);
       pw[4 + i / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(e[6], e[7], v, true);
     }
-    l_part = fmaf(lt, iw, l_part);
     const lds_char *Vl = (const lds_char *)vbuf;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -460,9 +499,11 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
         av[2 * t] = r2[0];
         av[2 * t + 1] = r2[1];
       }
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pw, oacc[db], 0, 0, 0, 127, 0,
+      // V's block scale rides on the A operand's e8m0 scale
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pw, oacc[db], 0, 0, 0, ve8, 0,
                                                                  127);
     }
+    lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pw, lacc, 0, 0, 0, 127, 0, 127);
   };
 
   auto end_step = [&]() {
@@ -498,10 +539,11 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- epilogue: O = (U/448) O^T / l, LSE = (m + log2 l) * ln 2
-  const float l_tot = xhalf_sum(l_part);
+  // ---- epilogue: O = O^T / l, LSE = (m + log2 l - kPShift) * ln 2, l = sum p' of the query
+  const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
+  const float l_tot = l32 < 16 ? ls0 : ls1;
   if (!qvalid) return;
-  const float inv = l_tot > 0.0f ? (U / 448.0f) / l_tot : 0.0f;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const Seg os = a.o[tile.q_kind];
   __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh;
 #pragma unroll
@@ -521,7 +563,7 @@ __global__ void __launch_bounds__(256, 3) attn_lowbit_kernel(const AttnArgs a) {
   if (lse && hl == 0) {
     // lse holds the smoothing shift scale * q.m written by the quantiser
     float *lp = lse + (int64_t)w.bh * a.q_rows[tile.q_kind] + qrow;
-    *lp = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f + *lp
+    *lp = l_tot > 0.0f ? (m_run + __log2f(l_tot) - kPShift) * 0.6931471805599453f + *lp
                        : -__builtin_inff();
   }
 }

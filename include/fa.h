@@ -124,7 +124,8 @@ typedef struct {
   fa_tensor o_tgt, o_src, o_ref;
   float *lse_tgt, *lse_src, *lse_ref;
   float *k_mean;   /* FA_LOWBIT quantiser: per-head channel mean [batch][heads][head_dim] */
-  float *v_absmax; /* FA_LOWBIT: largest V block scale of the call [batch][heads] */
+  float *v_absmax; /* FA_LOWBIT quantiser, optional (NULL = not kept): largest V block
+                      scale of the call [batch][heads]; fa_attn_fwd does not read it */
 } fa_io;
 
 typedef struct fa_layout fa_layout; /* opaque, immutable after build */
@@ -240,9 +241,11 @@ fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream
  *    (batch, head, 128-token block): scale = absmax/127, code =
  *    round_half_even(x * (127/absmax)), keys after subtracting m (exact for
  *    the softmax: q.m is constant along a row);
- *  - every V as OCP e4m3 per block: scale = absmax/448, round to nearest
- *    even, saturating; the largest V block scale per (batch, head) into
- *    out->v_absmax.
+ *  - every V as OCP e4m3 per block with a power-of-two scale: 2^e for the
+ *    smallest integer e >= -126 with 448 * 2^e >= absmax, codes x * 2^-e
+ *    rounded to nearest even (the attention kernel applies 2^e as the e8m0
+ *    block scale of its PV product); if out->v_absmax is non-NULL, the
+ *    largest V block scale per (batch, head) goes there.
  * Codes go to out->{q,k,v}_* .data (same strides as declared there), scales
  * to their .scale arrays.  Ring frames outside the call's view are not read.
  * Smoothing shifts every score of a row by scale*q.m, which leaves O unchanged
@@ -252,8 +255,8 @@ fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream
  * calls (or NULL to both).
  * FA_QUANT_RING_READY (needs FA_QUANT_MEAN_GIVEN): the ring's codes and scales in
  * out->k_ring / out->v_ring are kept up to date by fa_ring_quantize, with the same mean; the ring
- * is then not read or quantised here, and only the scales of its V blocks in view are folded
- * into v_absmax.  The per-call work is Q, the chunk, its source frames and the references.
+ * is then not read or quantised here (with a non-NULL v_absmax the scales of its V blocks in
+ * view are still folded into it).  The per-call work is Q, the chunk, its source frames and the references.
  */
 enum { FA_QUANT_MEAN_GIVEN = 1, FA_QUANT_RING_READY = 2 };
 fa_status fa_quantize_lowbit(const fa_layout *L, const fa_io *in, const fa_io *out, int32_t flags,

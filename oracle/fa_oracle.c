@@ -252,8 +252,19 @@ static void quant_blocks(const float *x, int N, int H, int D, const float *mean,
           const float a = fabsf(v);
           if (a > absmax) absmax = a;
         }
-      scale = absmax / qmax;
-      inv = absmax > 0.0f ? qmax / absmax : 0.0f;
+      if (is_fp8) {
+        /* power-of-two scale: absmax = f * 2^k with f in [0.5, 1); 448 * 2^e >= absmax holds
+         * from e = k - 9 on when f <= 448/512, else from e = k - 8 */
+        int k, e;
+        const float f = frexpf(absmax, &k);
+        e = k - 9 + (f > 0.875f ? 1 : 0);
+        if (e < -126) e = -126;
+        scale = absmax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+        inv = absmax > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+      } else {
+        scale = absmax / qmax;
+        inv = absmax > 0.0f ? qmax / absmax : 0.0f;
+      }
       scales[(long)h * nblk + b] = scale;
       for (t = t0; t < t1; ++t)
         for (d = 0; d < D; ++d) {
@@ -280,7 +291,7 @@ void fa_oracle_quant_int8(const float *x, int N, int H, int D, const float *mean
 
 void fa_oracle_quant_e4m3(const float *x, int N, int H, int D, const float *mean, uint8_t *codes,
                           float *scales) {
-  quant_blocks(x, N, H, D, mean, 448.0f, 1, codes, scales);
+  quant_blocks(x, N, H, D, mean, 0.0f, 1, codes, scales);
 }
 
 void fa_oracle_quant_int8_2d(const float *x, int rows, int cols, int br, int bc, int8_t *codes,

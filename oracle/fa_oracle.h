@@ -39,9 +39,9 @@
  * A row with no visible key gets o = 0 and lse = -inf.
  *
  * Per-block quantiser (the low-bit prologue): per (head, 128-token block)
- * symmetric int8 with scale absmax/127, and OCP e4m3 fp8 with scale
- * absmax/448, both round-to-nearest-even; K is first reduced by a per-head,
- * per-channel mean vector.
+ * symmetric int8 with scale absmax/127, and OCP e4m3 fp8 with a power-of-two
+ * scale (the smallest 2^e with 448 * 2^e >= absmax), both round-to-nearest-
+ * even; K is first reduced by a per-head, per-channel mean vector.
  */
 #ifndef FA_ORACLE_H
 #define FA_ORACLE_H
@@ -99,11 +99,13 @@ long fa_oracle_count(const fa_oracle_problem *p, int kind, int row);
 /*
  * Quantiser, one tensor [N][H][D] fp32.  For every head h and block
  * b = token/128: x' = x - mean[h][:] (mean may be NULL = zero), absmax over
- * the block's N_b*D values, scale = absmax/127 (int8) or absmax/448 (e4m3),
- * code = round_half_even(x' * (127/absmax)) clamped to +-127, or the e4m3
- * encoding of x' * (448/absmax).  An all-zero block gets scale 0 and codes 0.
- * The arithmetic is float32, with one division for each of scale and its
- * inverse, so a device can reproduce the codes bit for bit.
+ * the block's N_b*D values.  int8: scale = absmax/127, code =
+ * round_half_even(x' * (127/absmax)) clamped to +-127 (float32, one division
+ * for each of scale and its inverse).  e4m3: scale = 2^e for the smallest
+ * integer e >= -126 with 448 * 2^e >= absmax (exact, no division), code = the
+ * e4m3 encoding of x' * 2^-e, so the largest code lies in (224, 448].  An
+ * all-zero block gets scale 0 and codes 0.  A device reproduces the codes bit
+ * for bit.
  * codes: [N][H][D]; scales: [H][ceil(N/128)].
  */
 void fa_oracle_quant_int8(const float *x, int N, int H, int D, const float *mean,

@@ -546,14 +546,44 @@ def pin_quant_e4m3(lib):
     ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     got = np.array([O.e4m3_encode(float(v), lib=lib) for v in xs], np.uint8)
     _eq(got, ref, "e4m3 encoding vs torch float8_e4m3fn")
-    # block quantiser: the absmax element maps to +-448
-    x = g.standard_normal((200, 2, 8)).astype(np.float32)
+    # block quantiser: scale = the smallest power of two 2^e with 448 * 2^e >= absmax, codes the
+    # encodings of x / 2^e.  Hand-derived blocks (one head each, one block of 4 tokens):
+    # absmax 448 -> scale 1 (codes are the values' own encodings); 448.5 -> 2; 1 -> 2^-8 (448/256
+    # >= 1 > 448/512), the max maps to 256 (0x78); 0.875 -> 2^-9 exactly, the max maps to 448;
+    # just above 0.875 -> 2^-8, the max maps to 224 (0x76); all zero -> scale 0, codes 0;
+    # a subnormal absmax -> 2^-126 (the floor of e).
+    cases = [(448.0, 1.0, 0x7e), (448.5, 2.0, 0x76), (1.0, 2.0 ** -8, 0x78),
+             (0.875, 2.0 ** -9, 0x7e), (float(np.nextafter(np.float32(0.875), np.float32(1))),
+                                         2.0 ** -8, 0x76), (0.0, 0.0, 0x00), (1e-40, 2.0 ** -126, None)]
+    for amax, want_scale, want_code in cases:
+        x = np.zeros((4, 1, 8), np.float32)
+        x[1, 0, 3] = -amax if amax > 0 else 0.0
+        x[2, 0, 0] = np.float32(amax) * np.float32(0.3)
+        codes, scales = O.quant_e4m3(x, lib=lib)
+        assert scales[0, 0] == np.float32(want_scale), (amax, scales[0, 0], want_scale)
+        if want_code is not None:
+            assert codes[1, 0, 3] == (0x80 | want_code if amax > 0 else 0), (amax, hex(codes[1, 0, 3]))
+        if amax > 0:
+            assert codes[2, 0, 0] == O.e4m3_encode(float(np.float32(amax) * np.float32(0.3) /
+                                                         np.float32(want_scale)), lib=lib)
+        assert codes[0].max() == 0 and codes[3].max() == 0
+    # 448.5 / 2 = 224.25 encodes to 224 (0x76)
+    x = np.zeros((1, 1, 8), np.float32)
+    x[0, 0, 0] = 448.5
+    assert O.quant_e4m3(x, lib=lib)[0][0, 0, 0] == 0x76
+    # random blocks: power-of-two scales with 224 * s < absmax <= 448 * s, codes of x / s
+    x = (g.standard_normal((300, 2, 8)) * np.array([0.01, 40.0])[None, :, None]).astype(np.float32)
     codes, scales = O.quant_e4m3(x, lib=lib)
     for h in range(2):
-        blk = x[:128, h]
-        i = np.unravel_index(np.abs(blk).argmax(), blk.shape)
-        assert codes[:128, h][i] & 0x7f == 0x7e
-        assert scales[h, 0] == np.float32(np.abs(blk).max() / np.float32(448))
+        for b in range(3):
+            blk = x[b * 128:(b + 1) * 128, h]
+            s_ = float(scales[h, b])
+            am = float(np.abs(blk).max())
+            assert s_ > 0 and np.frexp(s_)[0] == 0.5, s_
+            assert 224 * s_ < am <= 448 * s_, (am, s_)
+            want = np.array([O.e4m3_encode(float(np.float32(v) / np.float32(s_)), lib=lib)
+                             for v in blk.ravel()[:64]], np.uint8)
+            _eq(codes[b * 128:(b + 1) * 128, h].ravel()[:64], want, "e4m3 block codes")
 
 
 def pin_kmean(lib):

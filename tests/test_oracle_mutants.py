@@ -44,6 +44,8 @@ MUTANTS = {
     "int8 truncation": ("float r = nearbyintf(y);", "float r = truncf(y);"),
     "int8 ties away": ("float r = nearbyintf(y);", "float r = roundf(y);"),
     "int8 scale inverted": ("scale = absmax / qmax;", "scale = qmax / absmax;"),
+    "e4m3 scale one power low": ("e = k - 9 + (f > 0.875f ? 1 : 0);", "e = k - 10 + (f > 0.875f ? 1 : 0);"),
+    "e4m3 scale boundary": ("(f > 0.875f ? 1 : 0)", "(f >= 0.875f ? 1 : 0)"),
     "e4m3 ties odd": ("(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
     "e4m3 bias 8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
                     "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
