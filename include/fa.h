@@ -233,7 +233,11 @@ fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream)
 fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
 
 /*
- * Low-bit prologue for an FA_LOWBIT layout.  From the bf16 tensors of `in`:
+ * Low-bit prologue for an FA_LOWBIT layout.  The pages name low-bit attention as part of the
+ * serving stack ("Vidu S2：全球领先的实时交互与实时编辑模型，正式发布", section "Vidu S2 背后的技术体系";
+ * "Vidu S2: Real-Time Interactive, Editable, and Spatial Video Generation", hybrid-attention
+ * paragraph) without fixing its arithmetic; the rules below are this library's reading.
+ * From the bf16 tensors of `in`:
  *  - a per-(batch, head) channel mean m of all keys the call reads (ring
  *    frames in view, chunk, source, references) into out->k_mean, or, with
  *    FA_QUANT_MEAN_GIVEN, m read from out->k_mean;
