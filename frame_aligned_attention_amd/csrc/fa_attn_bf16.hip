@@ -20,13 +20,16 @@
 // The block map picks the work-item height (the ping-pong kernel unless its
 // workgroups need more rounds over the chip than the 128-row ones).
 //
-// Per wave and key tile: 32 query rows,
-//   S^T (64 keys x 32 queries) = K_tile . Q^T   with v_mfma_f32_32x32x16_bf16,
-// so every lane holds one query column and 32 of its scores: the row max and
-// row sum are in-lane, plus one v_permlane32_swap between the lane halves.
-// Then O^T (D x 32) += V^T_tile . P^T, again 32x32x16 MFMAs.  P never leaves
-// registers: the S^T accumulator already is the B operand of the second
-// product once V^T's key order matches it.
+// Per wave and key tile: 32 query rows and keys as the M dimension,
+//   S^T (64 keys x 32 queries) = K_tile . Q^T,  then  O^T (D x 32) += V^T_tile . P^T.
+// The 4-wave kernel uses v_mfma_f32_32x32x16_bf16: every lane holds one query
+// column and 32 of its scores, so the row max and row sum are in-lane plus one
+// v_permlane32_swap between the lane halves.  The ping-pong kernel uses
+// v_mfma_f32_16x16x32_bf16 (a higher share of the matrix core's peak on gfx950):
+// a query's 64 scores sit in four lanes, reduced in-lane and by two lane swaps
+// (its layout is described at the kernel).  In both, P never leaves registers:
+// the S^T accumulator already is the B operand of the second product once V^T's
+// key order matches it.
 //
 // Memory.  K and V tiles go from HBM straight into LDS (buffer loads with
 // the LDS bit, 16 bytes per lane, no VGPR staging); the buffer descriptor of
