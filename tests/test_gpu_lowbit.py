@@ -176,6 +176,32 @@ def test_lowbit_attention_against_fp32_oracle(case):
         G.tol_check(o, ref[k][0], "lowbit", "lowbit %s rows" % G.KIND_NAMES[k], lse, ref[k][1])
 
 
+def test_lowbit_zero_and_tiny_v_blocks():
+    """Keys whose V block is all zero or tiny keep their softmax mass: the row sums run over the
+    e4m3 P itself, whatever V's block scale.  The reference image's V is zeroed (two whole
+    128-token blocks: about a third of a target row's keys, 256 of 736, and 256 of a source
+    row's 416) and the source frames' V is scaled by 1e-10 (block scales near 2^-40).  A row sum
+    that dropped the zero-V keys would scale O by ~1.5 and move the LSE by ~ln(2/3) = -0.4; the
+    bound holds it to the ordinary low-bit error."""
+    case = (61, 160, 2, 2, 0, 0, 0, [256], [0], 3)
+    G.say("case: low-bit attention, zero and tiny V blocks %s" % (case,))
+    seed, T, C, H, cs, win, cap, refs, t0s, qr = case
+    c = lowbit_call(seed, T, C, H, cs, win, cap, refs, t0s, qr)
+    c.v_ref = np.zeros_like(c.v_ref)
+    c.v_src = W.round_bf16(c.v_src * np.float32(1e-10))
+    run = LowbitRun(c)
+    run.quantize()
+    vs = run.scales["v_ref"].cpu().numpy()
+    assert np.all(vs == 0.0), "zero V blocks must get scale 0"
+    ss = run.scales["v_src"].cpu().numpy()
+    assert np.all((ss > 0) & (ss < 2.0 ** -30)), ss
+    res = run.attend()
+    ref = G.oracle_all(c)
+    for k, (o, lse) in res.items():
+        G.tol_check(o, ref[k][0], "lowbit", "lowbit zero/tiny V %s rows" % G.KIND_NAMES[k], lse,
+                    ref[k][1])
+
+
 def lowbit_stream_chunk_call(cs, H):
     """A chunk of the low-bit streaming workload (N(0,4) key offset) with its history."""
     w = W.WORKLOADS[4]
