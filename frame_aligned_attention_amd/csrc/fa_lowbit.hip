@@ -255,7 +255,7 @@ __device__ __forceinline__ int sw(int r) { return ((r >> 2) & 1) | (r & 2) | ((r
 // workgroups share a CU (32 KB of LDS each); the waves of the other one fill each wave's
 // dependency gaps.
 //
-// The softmax is VALU-bound, so three things keep VALU work off it:
+// Most of what a wave issues per tile is the softmax's VALU work, so three things cut it:
 //  - the int32 score accumulators start at the bits of the float kBias = 1.5 * 2^23: |q.k| <=
 //    128 * 127^2 < 2^22, so the sum's bits read as the float kBias + q.k exactly and no integer
 //    to float conversion is needed; kBias * fk is folded into the exp FMA (that term rounds
