@@ -48,8 +48,9 @@
 // Softmax.  Base-2 online softmax with scale*log2(e) folded into one FMA
 // before v_exp_f32.  The running max is raised only when a tile's max
 // exceeds it by more than 8 (so p <= 2^8): the O/l rescale is then rare.
-// Row sums are taken on the bf16-rounded p that feed the PV product
-// (v_dot2c_f32_bf16 against ones).
+// Row sums are taken on the bf16-rounded p that feed the PV product: the
+// 4-wave kernel with v_dot2c_f32_bf16 against ones, the ping-pong kernel on
+// the matrix core (a ones operand times P^T, in its matrix phase).
 #include <type_traits>
 
 #include "fa_device.h"
@@ -460,6 +461,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 //     32t + 4g + r and 32t + 16 + 4g + r, g = l/16), so P never leaves its
 //     lane; the A operand takes the same keys of channel cb*16 + l%16 from two
 //     transposing LDS reads.
+//   Row sums: L[qb] (16 x 16) += ones (16 x 32 keys) . P^T with the same B
+//     operands, so every row of L holds the 16 queries' sums and lane l reads
+//     its query's in place.  The softmax phase, which sets the pace, then has no
+//     row-sum arithmetic; the matrix phase has room for the four extra MFMAs.
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) {
   using Cfg = Bf16Cfg<D>;
@@ -598,9 +603,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // finite start: the first tile with any visible key always raises it, so -m_run is the exp
   // offset from then on with no test for -inf (a row with no visible key keeps l = 0)
   float m_run[2] = {-1e30f, -1e30f};
-  float l_part[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};  // row sums, two chains per query block
+  // row sums on the matrix core: D (16x16) += ones (16 x 32 keys) . P^T (32 keys x 16 queries)
+  // makes every row of D the row sums of the 16 queries, so lane l's lsum[qb] holds the sum of
+  // query qb*16 + l%16 (in all four elements)
+  f32x4_t lsum[2] = {f32x4_t{}, f32x4_t{}};
+  const bf16x8_t ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   const float c = a.c;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   f32x4_t s[4][2];  // S^T of the tile awaiting its softmax, [kb][qb]
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4_t{};
@@ -627,6 +636,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
         av, __builtin_bit_cast(bf16x8_t, pw[t][0]), oacc[cb][0], 0, 0, 0);
     oacc[cb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
         av, __builtin_bit_cast(bf16x8_t, pw[t][1]), oacc[cb][1], 0, 0, 0);
+  };
+  auto rowsum_step = [&](int t) {
+    lsum[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, __builtin_bit_cast(bf16x8_t, pw[t][0]),
+                                                      lsum[0], 0, 0, 0);
+    lsum[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, __builtin_bit_cast(bf16x8_t, pw[t][1]),
+                                                      lsum[1], 0, 0, 0);
   };
 
   // Matrix phase: S of the next tile (K in `kbuf`) and O += V P of this one (V in `vbuf`, P in
@@ -659,14 +674,16 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) pv_step(Vl, t, cb);
-    // operands seven MFMA pairs ahead (~220 cycles of matrix work, the LDS latency under this
+    rowsum_step(0);
+    rowsum_step(1);
+    // operands six MFMA pairs ahead (~190 cycles of matrix work, the LDS latency under this
     // load): K reads (one per QK pair), then V reads (two per PV pair).  Three pairs ahead was
-    // 2-3% slower.
-    constexpr int LA = 7;
+    // 2-3% slower; seven leaves too few registers beside the row-sum accumulators.
+    constexpr int LA = 6;
     __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS read: K operands of pairs 0..LA-1
 #pragma unroll
-    for (int i = 0; i < NQK + NPV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA pair (QK, then PV)
+    for (int i = 0; i < NQK + NPV + 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA pair (QK, then PV, then sums)
       if constexpr (decltype(with_loads)::value)
         if (i % EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       if (i + LA < NQK)
@@ -724,11 +741,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
         const bool need = mt > m_run[qb] + kThr;
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
         m_run[qb] = need ? mt : m_run[qb];
-        l_part[qb][0] *= alpha;
-        l_part[qb][1] *= alpha;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= alpha;
+          lsum[qb] *= alpha;
         }
         const float mneg = -m_run[qb];
 #pragma unroll
@@ -740,8 +756,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
                                  (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[1], c, mneg))};
             const bf16x2_t e1 = {(__bf16)__builtin_amdgcn_exp2f(fmaf(sv[2], c, mneg)),
                                  (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[3], c, mneg))};
-            l_part[qb][h2] = __builtin_amdgcn_fdot2_f32_bf16(e0, ones, l_part[qb][h2], false);
-            l_part[qb][h2] = __builtin_amdgcn_fdot2_f32_bf16(e1, ones, l_part[qb][h2], false);
             pw[t][qb][2 * h2] = __builtin_bit_cast(uint32_t, e0);
             pw[t][qb][2 * h2 + 1] = __builtin_bit_cast(uint32_t, e1);
           }
@@ -762,14 +776,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   auto pin_softmax = [&]() {
 #pragma unroll
     for (int t = 0; t < 2; ++t) __asm__ volatile("" : "+v"(pw[t][0]), "+v"(pw[t][1]));
-    __asm__ volatile("" : "+v"(l_part[0][0]), "+v"(l_part[0][1]), "+v"(l_part[1][0]),
-                     "+v"(l_part[1][1]), "+v"(m_run[0]), "+v"(m_run[1]));
+    __asm__ volatile("" : "+v"(m_run[0]), "+v"(m_run[1]));
   };
   auto pin_matrix = [&]() {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) __asm__ volatile("" : "+v"(s[kb][0]), "+v"(s[kb][1]));
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) __asm__ volatile("" : "+v"(oacc[cb][0]), "+v"(oacc[cb][1]));
+    __asm__ volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
   };
   // Neither barrier may have arithmetic moved across it (the machine scheduler would otherwise
   // pull the exp work of a softmax phase into the neighbouring matrix phase).
@@ -882,7 +896,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   float *lse = a.lse[tile.q_kind];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = x16_sum(xhalf_sum(l_part[qb][0] + l_part[qb][1]));
+    const float l_tot = lsum[qb][0];
     if (!qvalid[qb]) continue;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     __bf16 *op = (__bf16 *)os.p + b * os.sb + (int64_t)qrow[qb] * os.sn + h * os.sh;
