@@ -23,6 +23,7 @@ FA_MAX_REF = 8
 FA_SEG_RING, FA_SEG_TGT, FA_SEG_SRC, FA_SEG_REF = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_SAME_FRAME, FA_MASK_GATE = 0, 1, 2
 FA_QUANT_MEAN_GIVEN, FA_QUANT_RING_READY = 1, 2
+FA_KEY_SPLIT_AUTO, FA_KEY_SPLIT_OFF = 0, 1
 
 
 class fa_layout_desc(C.Structure):
@@ -31,7 +32,7 @@ class fa_layout_desc(C.Structure):
                 ("chunk_start", C.c_int32), ("window", C.c_int32), ("cache_frames", C.c_int32),
                 ("query_rows", C.c_int32), ("batch", C.c_int32), ("heads", C.c_int32),
                 ("head_dim", C.c_int32), ("dtype", C.c_int32), ("scale", C.c_float),
-                ("sink_frames", C.c_int32), ("block_rows", C.c_int32)]
+                ("sink_frames", C.c_int32), ("block_rows", C.c_int32), ("key_split", C.c_int32)]
 
 
 class fa_tensor(C.Structure):
@@ -86,6 +87,10 @@ def _load():
         "fa_layout_tiles": ([P] + [C.POINTER(C.c_int32)] * 3, C.c_int),
         "fa_layout_tile": ([P, C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
                             C.c_int32], C.c_int),
+        "fa_layout_splits": ([P, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
+        "fa_layout_split": ([P, C.c_int32] + [C.POINTER(C.c_int32)] * 3 +
+                            [C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
+                             C.c_int32], C.c_int),
         "fa_layout_destroy": ([P], C.c_int),
         "fa_layout_prepare": ([P], C.c_int),
         "fa_attn_fwd": ([P, C.POINTER(fa_io), P], C.c_int),
@@ -148,7 +153,7 @@ def make_desc(frames: int, tokens_per_frame: int, heads: int, head_dim: int, *, 
               ref_tokens: Sequence[int] = (), ref_t0: Sequence[int] = (), chunk_start: int = 0,
               window: int = 0, cache_frames: int = 0, query_rows: int = FA_Q_TARGET,
               dtype: int = FA_BF16, scale: float = 0.0, sink_frames: int = 0,
-              block_rows: int = 0) -> fa_layout_desc:
+              block_rows: int = 0, key_split: int = FA_KEY_SPLIT_AUTO) -> fa_layout_desc:
     d = fa_layout_desc()
     d.frames, d.tokens_per_frame = frames, tokens_per_frame
     d.n_ref = len(ref_tokens)
@@ -159,6 +164,7 @@ def make_desc(frames: int, tokens_per_frame: int, heads: int, head_dim: int, *, 
     d.dtype, d.scale = dtype, scale
     d.sink_frames = sink_frames
     d.block_rows = block_rows
+    d.key_split = key_split
     return d
 
 
@@ -231,6 +237,29 @@ def fa_layout_tile(L: Layout, i: int):
     _check(lib.fa_layout_tile(L.handle, i, C.byref(t), rr, 64), "fa_layout_tile")
     ranges = [(r.seg, r.begin, r.end, r.mask, r.param) for r in rr[:t.n_ranges]]
     return (t.q_kind, t.row0, t.rows), ranges
+
+
+def fa_layout_splits(L: Layout):
+    """(split work items, key parts in total)."""
+    n, parts = C.c_int32(), C.c_int32()
+    _check(lib.fa_layout_splits(L.handle, C.byref(n), C.byref(parts)), "fa_layout_splits")
+    return n.value, parts.value
+
+
+def fa_layout_split(L: Layout, s: int):
+    """Split item s: (tile, batch*heads + head, [(part tile, part ranges), ...])."""
+    tile, bh, parts = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib.fa_layout_split(L.handle, s, C.byref(tile), C.byref(bh), C.byref(parts), -1, None,
+                               None, 0), "fa_layout_split")
+    out = []
+    for p in range(parts.value):
+        t = fa_tile_info()
+        rr = (fa_range_info * 64)()
+        _check(lib.fa_layout_split(L.handle, s, None, None, None, p, C.byref(t), rr, 64),
+               "fa_layout_split")
+        out.append(((t.q_kind, t.row0, t.rows),
+                    [(r.seg, r.begin, r.end, r.mask, r.param) for r in rr[:t.n_ranges]]))
+    return tile.value, bh.value, out
 
 
 def fa_layout_destroy(L: Layout):

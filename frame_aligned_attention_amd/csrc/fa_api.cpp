@@ -121,6 +121,9 @@ fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
   a.tiles = m.tiles;
   a.ranges = m.ranges;
   a.work = m.work;
+  a.ws = m.ws;
+  a.splits = m.splits;
+  if (!L->splits.empty() && !m.ws) return fail(FA_ERR_INVALID, "split layout without a workspace");
   const int grid = (int)L->work.size();
   hipError_t e;
   if (d.dtype == FA_F32)
@@ -130,6 +133,11 @@ fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
   else
     e = launch_attn_lowbit(a, d.head_dim, grid, stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  if (!L->splits.empty()) {
+    e = launch_merge_parts(a, d.head_dim, (int)L->splits.size(), stream);
+    if (e != hipSuccess)
+      return fail(FA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  }
   return FA_OK;
 }
 
@@ -439,7 +447,8 @@ namespace fa {
 
 static bool same_map(const fa_layout *a, const fa_layout *b) {
   if (a->tiles.size() != b->tiles.size() || a->ranges.size() != b->ranges.size() ||
-      a->work.size() != b->work.size())
+      a->work.size() != b->work.size() || a->splits.size() != b->splits.size() ||
+      a->n_tiles != b->n_tiles || a->block_m != b->block_m)
     return false;
   // descriptors may differ only in chunk_start / ref_t0, both folded into the ranges
   fa_layout_desc x = a->d, y = b->d;
@@ -448,7 +457,9 @@ static bool same_map(const fa_layout *a, const fa_layout *b) {
   if (std::memcmp(&x, &y, sizeof(fa_layout_desc)) != 0) return false;
   return std::memcmp(a->tiles.data(), b->tiles.data(), a->tiles.size() * sizeof(DevTile)) == 0 &&
          std::memcmp(a->ranges.data(), b->ranges.data(), a->ranges.size() * sizeof(DevRange)) == 0 &&
-         std::memcmp(a->work.data(), b->work.data(), a->work.size() * sizeof(DevWork)) == 0;
+         std::memcmp(a->work.data(), b->work.data(), a->work.size() * sizeof(DevWork)) == 0 &&
+         (a->splits.empty() ||
+          std::memcmp(a->splits.data(), b->splits.data(), a->splits.size() * sizeof(DevSplit)) == 0);
 }
 
 // Layout of the chunk at s->next_frame, shared with an earlier chunk when the block map is the

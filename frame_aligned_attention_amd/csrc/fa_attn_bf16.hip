@@ -892,6 +892,32 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.  A query's row sum is spread over
   // its four lanes; lane l16 + 16*g4 stores channels cb*16 + 4*g4 .. +3 of its query.
+  if (tile.ws) {
+    // One key part of a split work item: its normalised O in fp32, rows of D floats, and its
+    // LSE go to workspace slot ws - 1; merge_parts_kernel writes the item's O and LSE.
+    float *slot = a.ws + (int64_t)(tile.ws - 1) * ws_slot_floats(D);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l_tot = lsum[qb][0];
+      if (!qvalid[qb]) continue;
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const int qloc = qrow[qb] - tile.row0;
+      float *op = slot + qloc * D;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        f32x4_t v;
+        v[0] = oacc[cb][qb][0] * inv;
+        v[1] = oacc[cb][qb][1] * inv;
+        v[2] = oacc[cb][qb][2] * inv;
+        v[3] = oacc[cb][qb][3] * inv;
+        *(f32x4_t *)(op + cb * 16 + 4 * g4) = v;
+      }
+      if (g4 == 0)
+        slot[kBf16PPBlockM * D + qloc] =
+            l_tot > 0.0f ? (m_run[qb] + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
+    }
+    return;
+  }
   const Seg os = a.o[tile.q_kind];
   float *lse = a.lse[tile.q_kind];
 #pragma unroll
@@ -914,6 +940,59 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
       lse[(int64_t)w.bh * a.q_rows[tile.q_kind] + qrow[qb]] =
           l_tot > 0.0f ? (m_run[qb] + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
   }
+}
+
+// Merge of a split work item's key parts.  Part i left, for each row, its normalised O_i and
+// LSE_i over its own keys; over all the item's keys LSE = log sum_i exp(LSE_i) and
+// O = sum_i exp(LSE_i - LSE) O_i (parts in which a row sees no key have LSE_i = -inf and
+// weigh nothing).  D/4 threads share a row, four channels each; a workgroup covers 1024/D rows
+// and D/4 workgroups one item's 256 rows.
+template <int D>
+__global__ void __launch_bounds__(256) merge_parts_kernel(const AttnArgs a) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR, BPI = kBf16PPBlockM / RPB;
+  constexpr int64_t SF = ws_slot_floats(D);
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const int s = blockIdx.x / BPI;
+  const DevSplit sp = a.splits[s];
+  const DevTile tile = a.tiles[sp.tile];
+  const int r = (blockIdx.x - s * BPI) * RPB + (int)threadIdx.x / TPR;
+  const int c = ((int)threadIdx.x % TPR) * 4;
+  if (r >= tile.rows) return;
+  const float *base = a.ws + (int64_t)sp.slot0 * SF;
+  float m = -__builtin_inff();
+  for (int p = 0; p < sp.parts; ++p) m = fmaxf(m, base[p * SF + kBf16PPBlockM * D + r]);
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float l = 0.0f;
+  if (m > -__builtin_inff()) {
+    for (int p = 0; p < sp.parts; ++p) {
+      const float wgt = __expf(base[p * SF + kBf16PPBlockM * D + r] - m);
+      const f32x4_t o = *(const f32x4_t *)(base + p * SF + (int64_t)r * D + c);
+      l += wgt;
+      acc += wgt * o;
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const int b = sp.bh / a.H, h = sp.bh - (sp.bh / a.H) * a.H;
+  const int qrow = tile.row0 + r;
+  const Seg os = a.o[tile.q_kind];
+  bf16x4_t v;
+  v[0] = (__bf16)(acc[0] * inv);
+  v[1] = (__bf16)(acc[1] * inv);
+  v[2] = (__bf16)(acc[2] * inv);
+  v[3] = (__bf16)(acc[3] * inv);
+  *(bf16x4_t *)((__bf16 *)os.p + b * os.sb + (int64_t)qrow * os.sn + h * os.sh + c) = v;
+  float *lse = a.lse[tile.q_kind];
+  if (lse && c == 0)
+    lse[(int64_t)sp.bh * a.q_rows[tile.q_kind] + qrow] = l > 0.0f ? m + __logf(l) : -__builtin_inff();
+}
+
+hipError_t launch_merge_parts(const AttnArgs &a, int head_dim, int n_split, hipStream_t s) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL(merge_parts_kernel<64>, dim3(n_split * 16), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_parts_kernel<128>, dim3(n_split * 32), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int block_m, int grid,

@@ -31,15 +31,32 @@ struct DevRange {
   int32_t pad[3];
 };
 
-// One tile of query rows.  Ranges [r_begin, r_begin + r_count) of the map.
+// One tile of query rows.  Ranges [r_begin, r_begin + r_count) of the map.  ws = 0: the
+// kernel writes the tile's O and LSE; ws = s + 1: the tile is one key part of a split work item
+// and the kernel writes its normalised fp32 O and its LSE to workspace slot s instead.
 struct DevTile {
   int32_t q_kind;
   int32_t row0;
   int32_t rows;
   int32_t r_begin;
   int32_t r_count;
-  int32_t pad[3];
+  int32_t ws;
+  int32_t pad[2];
 };
+
+// A work item whose keys were split: the base tile, its (batch*heads + head), and the `parts`
+// workspace slots slot0 .. slot0 + parts - 1 the merge combines into its O and LSE.
+struct DevSplit {
+  int32_t tile;
+  int32_t bh;
+  int32_t slot0;
+  int32_t parts;
+};
+
+// Workspace slot of a key part (ping-pong kernel rows): O as fp32 [256][D], then LSE [256].
+constexpr int64_t ws_slot_floats(int head_dim) { return int64_t(256) * (head_dim + 1); }
+constexpr int kMaxKeyParts = 16;  // parts per split work item
+constexpr int kMaxWsSlots = 256;  // slots per layout (the split parts fill at most one round)
 
 // Grid slot -> (tile, batch*heads + head); tile < 0 marks an idle slot.
 struct DevWork {
@@ -70,6 +87,8 @@ struct AttnArgs {
   const DevTile *tiles;
   const DevRange *ranges;
   const DevWork *work;
+  float *ws;                 // key-part workspace (slots of ws_slot_floats(D) floats)
+  const DevSplit *splits;    // split work items, for the merge
 };
 
 struct RingArgs {
@@ -91,6 +110,8 @@ __host__ __device__ inline int ring_slot(int g, int sink, int cache_frames) {
 // Launchers (defined in the .hip files); return hipError_t of the launch.
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, int block_m, int grid,
                             hipStream_t s);
+// Combines the key parts of n_split split work items into their O and LSE.
+hipError_t launch_merge_parts(const AttnArgs &a, int head_dim, int n_split, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_attn_lowbit(const AttnArgs &a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_ring_append(const RingArgs &a, hipStream_t s);

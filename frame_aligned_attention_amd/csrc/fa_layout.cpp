@@ -37,6 +37,8 @@ static fa_status validate(const fa_layout_desc *d, int32_t ring_first, int32_t *
   if (d->block_rows != 0 && (d->dtype != FA_BF16 || (d->block_rows != kBf16BlockM &&
                                                       d->block_rows != kBf16PPBlockM)))
     return fail(FA_ERR_INVALID, "block_rows must be 0, or 128 or 256 with FA_BF16");
+  if (d->key_split != FA_KEY_SPLIT_AUTO && d->key_split != FA_KEY_SPLIT_OFF)
+    return fail(FA_ERR_INVALID, "key_split must be FA_KEY_SPLIT_AUTO or FA_KEY_SPLIT_OFF");
   if (d->query_rows <= 0 || d->query_rows > 7)
     return fail(FA_ERR_INVALID, "query_rows must be a non-empty set of FA_Q_* bits");
   if (d->batch < 1 || d->heads < 1) return fail(FA_ERR_INVALID, "batch and heads must be >= 1");
@@ -107,26 +109,99 @@ static void add_ref_ranges(const fa_layout_desc *d, int fa_rel, int fb_rel,
   }
 }
 
-// Query rows per bf16 work item when the caller leaves it open.  The 256-row kernel runs one
-// workgroup per CU, the 128-row kernel two: take 256 unless its workgroups need more rounds
-// over the chip's 256 CUs than the 128-row ones do (a nearly empty last round costs more than
-// the ping-pong kernel gains).
-static int32_t bf16_block_rows(const fa_layout_desc &d) {
-  constexpr int64_t kCUs = 256;
-  auto items = [&](int64_t bm) {
-    const int64_t F = d.frames, T = d.tokens_per_frame;
-    int64_t ref = 0;
-    for (int r = 0; r < d.n_ref; ++r) ref += d.ref_tokens[r];
-    int64_t n = 0;
-    if (d.query_rows & FA_Q_TARGET) n += (F * T + bm - 1) / bm;
-    if (d.query_rows & FA_Q_SOURCE) n += (F * T + bm - 1) / bm;
-    if (d.query_rows & FA_Q_REF) n += (ref + bm - 1) / bm;
-    return n * d.batch * d.heads;
-  };
-  const int64_t r256 = (items(kBf16PPBlockM) + kCUs - 1) / kCUs;
-  const int64_t r128 = (items(kBf16BlockM) + 2 * kCUs - 1) / (2 * kCUs);
-  return r256 <= r128 ? kBf16PPBlockM : kBf16BlockM;
+// Keys of a tile in the kernels' 64-key steps, range by range.
+static int64_t tile_steps(const fa_layout *L, const DevTile &t) {
+  int64_t n = 0;
+  for (int j = 0; j < t.r_count; ++j) {
+    const DevRange &r = L->ranges[t.r_begin + j];
+    if (r.end > r.begin) n += (r.end - r.begin + kBf16BlockN - 1) / kBf16BlockN;
+  }
+  return n;
 }
+
+// Key split of the ping-pong kernel's last round.  That kernel runs one workgroup per CU, so N
+// work items take ceil(N / 256) rounds, and when the last round holds few items as costly as
+// the others, most of the chip idles through it.  Each such item is cut into parts along its
+// 64-key steps (a part's sub-ranges keep their range's mask, which depends on absolute key and
+// row positions only); the parts run on the idle CUs, write normalised O and LSE to workspace
+// slots, and a merge kernel combines them with log-sum-exp weights.  Returns the length of the
+// last round in rounds as the split leaves it (1 when nothing is split).
+static constexpr int64_t kMinPartSteps = 8;  // 512 keys: below that a part's fixed costs dominate
+static double split_last_round(fa_layout *L) {
+  constexpr int64_t kCUs = 256;
+  std::vector<int> live;  // grid slots of work items
+  for (int j = 0; j < (int)L->work.size(); ++j)
+    if (L->work[j].tile >= 0) live.push_back(j);
+  const int64_t n = (int64_t)live.size();
+  if (n == 0 || L->d.key_split == FA_KEY_SPLIT_OFF) return 1.0;
+  const int64_t rounds = (n + kCUs - 1) / kCUs, tail = n - kCUs * (rounds - 1);
+  std::vector<int64_t> steps(L->tiles.size());
+  int64_t max_steps = 0;
+  for (size_t i = 0; i < L->tiles.size(); ++i) {
+    steps[i] = tile_steps(L, L->tiles[i]);
+    max_steps = std::max(max_steps, steps[i]);
+  }
+  // Items of the last round costing half the largest item or more are split; the rest of the
+  // round (cheaper kinds of query rows) runs as it is.
+  std::vector<int> cut;
+  int64_t other = 0;
+  for (int64_t i = n - tail; i < n; ++i) {
+    const int64_t st = steps[L->work[live[i]].tile];
+    if (2 * st >= max_steps && st >= 2 * kMinPartSteps)
+      cut.push_back(live[i]);
+    else
+      other = std::max(other, st);
+  }
+  if (cut.empty()) return 1.0;
+  const int64_t room = kCUs - (tail - (int64_t)cut.size());
+  const int64_t P = std::min<int64_t>(kMaxKeyParts, room / (int64_t)cut.size());
+  if (P < 2) return 1.0;
+  double last = (double)other / (double)max_steps;
+  int slot = 0;
+  for (int j : cut) {
+    const DevWork w = L->work[j];
+    const DevTile base = L->tiles[w.tile];  // a copy: `tiles` grows below
+    const int64_t nb = steps[w.tile];
+    const int64_t parts = std::min<int64_t>(P, nb / kMinPartSteps);
+    last = std::max(last, (double)((nb + parts - 1) / parts) / (double)max_steps);
+    L->splits.push_back(DevSplit{w.tile, w.bh, slot, (int32_t)parts});
+    // part p takes steps [p*nb/parts, (p+1)*nb/parts) of the tile's range sequence
+    int r = 0;        // range of the tile being handed out
+    int64_t k = 0;    // its steps already handed out
+    for (int64_t p = 0; p < parts; ++p) {
+      int64_t want = (p + 1) * nb / parts - p * nb / parts;
+      DevTile t = base;
+      t.r_begin = (int32_t)L->ranges.size();
+      t.ws = slot + (int32_t)p + 1;
+      while (want > 0 && r < base.r_count) {
+        const DevRange src = L->ranges[base.r_begin + r];  // a copy: `ranges` grows below
+        const int64_t rs =
+            src.end > src.begin ? (src.end - src.begin + kBf16BlockN - 1) / kBf16BlockN : 0;
+        if (k >= rs) {
+          ++r;
+          k = 0;
+          continue;
+        }
+        const int64_t take = std::min(want, rs - k);
+        DevRange sub = src;
+        sub.begin = (int32_t)(src.begin + k * kBf16BlockN);
+        sub.end = (int32_t)std::min<int64_t>(src.end, src.begin + (k + take) * kBf16BlockN);
+        L->ranges.push_back(sub);
+        k += take;
+        want -= take;
+      }
+      t.r_count = (int32_t)L->ranges.size() - t.r_begin;
+      L->work.push_back(DevWork{(int32_t)L->tiles.size(), w.bh});
+      L->tiles.push_back(t);
+    }
+    slot += (int)parts;
+    L->work[j] = DevWork{-1, 0};
+  }
+  L->ws_slots = slot;
+  return last;
+}
+
+static void fill_map(fa_layout *L, const std::vector<DevRange> &ring_runs);
 
 static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout *L) {
   int32_t hist_lo = 0, rf = 0;
@@ -140,7 +215,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   L->hist_lo = hist_lo;
   const int T = d.tokens_per_frame, F = d.frames, cs = d.chunk_start;
   L->block_m = d.dtype == FA_F32 ? kF32BlockM : d.dtype == FA_BF16 ? kBf16BlockM : kLowbitBlockM;
-  if (d.dtype == FA_BF16) L->block_m = d.block_rows ? d.block_rows : bf16_block_rows(d);
+  if (d.dtype == FA_BF16) L->block_m = d.block_rows ? d.block_rows : kBf16PPBlockM;
   L->block_n = d.dtype == FA_F32 ? kF32BlockN : d.dtype == FA_BF16 ? kBf16BlockN : kLowbitBlockN;
   int ref_total = 0;
   for (int r = 0; r < d.n_ref; ++r) ref_total += d.ref_tokens[r];
@@ -170,6 +245,42 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
     }
   }
 
+  fill_map(L, ring_runs);
+  if (d.dtype == FA_BF16 && L->block_m == kBf16PPBlockM) {
+    int64_t live = 0;
+    for (const DevWork &w : L->work) live += w.tile >= 0;
+    const double last = split_last_round(L);
+    if (d.block_rows == 0) {
+      // 256 rows unless the 128-row kernel (two workgroups per CU) needs clearly fewer rounds
+      // over the chip's 256 CUs, the split part of a last round counting as its fraction of a
+      // round.  The 256-row kernel runs a round of the same rows ~9% faster (3600-token chunk:
+      // 4 rounds of either), hence the 0.95.
+      const int64_t rounds = (live + 255) / 256;
+      const double pp = (double)(rounds > 0 ? rounds - 1 : 0) + (rounds > 0 ? last : 0.0);
+      int64_t items = 0;
+      for (int k = 0; k < 3; ++k) items += (L->q_rows[k] + kBf16BlockM - 1) / kBf16BlockM;
+      items *= (int64_t)d.batch * d.heads;
+      const int64_t r128 = (items + 511) / 512;
+      if (0.95 * pp > (double)r128) {
+        L->tiles.clear();
+        L->ranges.clear();
+        L->work.clear();
+        L->splits.clear();
+        L->ws_slots = 0;
+        L->block_m = kBf16BlockM;
+        fill_map(L, ring_runs);
+      }
+    }
+  }
+  return FA_OK;
+}
+
+// Tiles and key ranges of the block map at L->block_m rows per tile, the work counts, and the
+// work order.
+static void fill_map(fa_layout *L, const std::vector<DevRange> &ring_runs) {
+  const fa_layout_desc &d = L->d;
+  const int T = d.tokens_per_frame, F = d.frames, cs = d.chunk_start;
+  const int ref_total = L->ref_total, hist_frames = L->hist_frames;
   const int BM = L->block_m;
   for (int kind = 0; kind < 3; ++kind) {
     const int rows = L->q_rows[kind];
@@ -196,6 +307,7 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
       L->tiles.push_back(t);
     }
   }
+  L->n_tiles = (int32_t)L->tiles.size();
 
   // Work counts.
   const double BH = (double)d.batch * d.heads;
@@ -266,7 +378,6 @@ static fa_status build(const fa_layout_desc *din, int32_t ring_first, fa_layout 
   L->work.assign(maxlen * 8, DevWork{-1, 0});
   for (size_t x = 0; x < 8; ++x)
     for (size_t j = 0; j < xcd[x].size(); ++j) L->work[j * 8 + x] = xcd[x][j];
-  return FA_OK;
 }
 
 fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload) {
@@ -284,29 +395,35 @@ fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload) {
                 "before capturing the stream");
   DeviceMap m;
   const size_t nt = std::max<size_t>(1, L->tiles.size()), nr = std::max<size_t>(1, L->ranges.size()),
-               nw = std::max<size_t>(1, L->work.size());
-  if (hipMalloc(&m.tiles, nt * sizeof(DevTile)) != hipSuccess ||
-      hipMalloc(&m.ranges, nr * sizeof(DevRange)) != hipSuccess ||
-      hipMalloc(&m.work, nw * sizeof(DevWork)) != hipSuccess) {
-    (void)hipGetLastError();
+               nw = std::max<size_t>(1, L->work.size()), ns = std::max<size_t>(1, L->splits.size());
+  const size_t wsb = ws_bytes(L);
+  auto free_all = [&]() {
     if (m.tiles) (void)hipFree(m.tiles);
     if (m.ranges) (void)hipFree(m.ranges);
+    if (m.work) (void)hipFree(m.work);
+    if (m.splits) (void)hipFree(m.splits);
+    if (m.ws) (void)hipFree(m.ws);
+  };
+  if (hipMalloc(&m.tiles, nt * sizeof(DevTile)) != hipSuccess ||
+      hipMalloc(&m.ranges, nr * sizeof(DevRange)) != hipSuccess ||
+      hipMalloc(&m.work, nw * sizeof(DevWork)) != hipSuccess ||
+      hipMalloc(&m.splits, ns * sizeof(DevSplit)) != hipSuccess ||
+      (wsb && hipMalloc(&m.ws, wsb) != hipSuccess)) {
+    (void)hipGetLastError();
+    free_all();
     return fail(FA_ERR_NOMEM, "device allocation of the block map failed");
   }
   bool ok = true;
-  if (!L->tiles.empty())
-    ok &= hipMemcpy(m.tiles, L->tiles.data(), L->tiles.size() * sizeof(DevTile),
-                    hipMemcpyHostToDevice) == hipSuccess;
-  if (!L->ranges.empty())
-    ok &= hipMemcpy(m.ranges, L->ranges.data(), L->ranges.size() * sizeof(DevRange),
-                    hipMemcpyHostToDevice) == hipSuccess;
-  if (!L->work.empty())
-    ok &= hipMemcpy(m.work, L->work.data(), L->work.size() * sizeof(DevWork),
-                    hipMemcpyHostToDevice) == hipSuccess;
+  auto put = [&](void *dst, const void *src, size_t bytes) {
+    if (bytes) ok &= hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice) == hipSuccess;
+  };
+  put(m.tiles, L->tiles.data(), L->tiles.size() * sizeof(DevTile));
+  put(m.ranges, L->ranges.data(), L->ranges.size() * sizeof(DevRange));
+  put(m.work, L->work.data(), L->work.size() * sizeof(DevWork));
+  put(m.splits, L->splits.data(), L->splits.size() * sizeof(DevSplit));
   if (!ok) {
-    (void)hipFree(m.tiles);
-    (void)hipFree(m.ranges);
-    (void)hipFree(m.work);
+    (void)hipGetLastError();
+    free_all();
     return fail(FA_ERR_HIP, "uploading the block map failed");
   }
   L->dev[dev] = m;
@@ -314,18 +431,25 @@ fa_status device_map(const fa_layout *L, DeviceMap *out, bool may_upload) {
   return FA_OK;
 }
 
+size_t ws_bytes(const fa_layout *L) {
+  return (size_t)L->ws_slots * (size_t)ws_slot_floats(L->d.head_dim) * sizeof(float);
+}
+
 }  // namespace fa
 
 using namespace fa;
 
 namespace fa {
-size_t map_image_bytes(const fa_layout *L, size_t *off_ranges, size_t *off_work) {
+size_t map_image_bytes(const fa_layout *L, size_t *off_ranges, size_t *off_work,
+                       size_t *off_splits) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t r = up(L->tiles.size() * sizeof(DevTile));
   const size_t w = r + up(L->ranges.size() * sizeof(DevRange));
+  const size_t sp = w + up(L->work.size() * sizeof(DevWork));
   if (off_ranges) *off_ranges = r;
   if (off_work) *off_work = w;
-  return w + up(L->work.size() * sizeof(DevWork));
+  if (off_splits) *off_splits = sp;
+  return sp + up(L->splits.size() * sizeof(DevSplit));
 }
 }  // namespace fa
 
@@ -338,8 +462,8 @@ extern "C" fa_status fa_layout_prepare(const fa_layout *L) {
   // pinned host image of the block map, the source of fa_attn_fwd_noalloc's per-call copy
   std::lock_guard<std::mutex> g(L->mu);
   if (!L->pinned) {
-    size_t orr = 0, ow = 0;
-    const size_t bytes = map_image_bytes(L, &orr, &ow);
+    size_t orr = 0, ow = 0, osp = 0;
+    const size_t bytes = map_image_bytes(L, &orr, &ow, &osp);
     char *p = nullptr;
     if (hipHostMalloc((void **)&p, bytes, hipHostMallocDefault) != hipSuccess) {
       (void)hipGetLastError();
@@ -349,9 +473,12 @@ extern "C" fa_status fa_layout_prepare(const fa_layout *L) {
     std::memcpy(p, L->tiles.data(), L->tiles.size() * sizeof(DevTile));
     std::memcpy(p + orr, L->ranges.data(), L->ranges.size() * sizeof(DevRange));
     std::memcpy(p + ow, L->work.data(), L->work.size() * sizeof(DevWork));
+    if (!L->splits.empty())
+      std::memcpy(p + osp, L->splits.data(), L->splits.size() * sizeof(DevSplit));
     fa_layout *M = const_cast<fa_layout *>(L);
     M->off_ranges = orr;
     M->off_work = ow;
+    M->off_splits = osp;
     L->pinned_bytes = bytes;
     L->pinned = p;
   }
@@ -391,23 +518,53 @@ extern "C" fa_status fa_layout_stats(const fa_layout *L, double *useful_pairs, d
 extern "C" fa_status fa_layout_tiles(const fa_layout *L, int32_t *n_tiles, int32_t *block_m,
                                      int32_t *block_n) {
   if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
-  if (n_tiles) *n_tiles = (int32_t)L->tiles.size();
+  if (n_tiles) *n_tiles = L->n_tiles;
   if (block_m) *block_m = L->block_m;
   if (block_n) *block_n = L->block_n;
   return FA_OK;
 }
 
-extern "C" fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile,
-                                    fa_range_info *ranges, int32_t cap) {
-  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
-  if (i < 0 || i >= (int32_t)L->tiles.size()) return fail(FA_ERR_INVALID, "tile index out of range");
-  const DevTile &t = L->tiles[i];
+static void copy_tile(const fa_layout *L, const DevTile &t, fa_tile_info *tile,
+                      fa_range_info *ranges, int32_t cap) {
   if (tile) *tile = fa_tile_info{t.q_kind, t.row0, t.rows, t.r_count};
   if (ranges)
     for (int j = 0; j < t.r_count && j < cap; ++j) {
       const DevRange &r = L->ranges[t.r_begin + j];
       ranges[j] = fa_range_info{r.seg, r.begin, r.end, r.mask, r.param};
     }
+}
+
+extern "C" fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile,
+                                    fa_range_info *ranges, int32_t cap) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (i < 0 || i >= L->n_tiles) return fail(FA_ERR_INVALID, "tile index out of range");
+  copy_tile(L, L->tiles[i], tile, ranges, cap);
+  return FA_OK;
+}
+
+extern "C" fa_status fa_layout_splits(const fa_layout *L, int32_t *n_split, int32_t *n_parts) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (n_split) *n_split = (int32_t)L->splits.size();
+  if (n_parts) *n_parts = L->ws_slots;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_layout_split(const fa_layout *L, int32_t s, int32_t *tile, int32_t *bh,
+                                     int32_t *parts, int32_t p, fa_tile_info *part,
+                                     fa_range_info *ranges, int32_t cap) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (s < 0 || s >= (int32_t)L->splits.size())
+    return fail(FA_ERR_INVALID, "split index out of range");
+  const DevSplit &sp = L->splits[s];
+  if (p < -1 || p >= sp.parts) return fail(FA_ERR_INVALID, "part index out of range");
+  if (tile) *tile = sp.tile;
+  if (bh) *bh = sp.bh;
+  if (parts) *parts = sp.parts;
+  if (p >= 0) {
+    // the part tiles follow the block map's tiles in slot order
+    const int32_t ti = L->n_tiles + sp.slot0 + p;
+    copy_tile(L, L->tiles[ti], part, ranges, cap);
+  }
   return FA_OK;
 }
 
@@ -423,6 +580,8 @@ extern "C" fa_status fa_layout_destroy(fa_layout *L) {
         (void)hipFree(kv.second.tiles);
         (void)hipFree(kv.second.ranges);
         (void)hipFree(kv.second.work);
+        (void)hipFree(kv.second.splits);
+        if (kv.second.ws) (void)hipFree(kv.second.ws);
       }
       (void)hipSetDevice(cur);
     }

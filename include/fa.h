@@ -97,7 +97,14 @@ typedef struct {
                                ping-pong kernel); 0 = chosen from the grid (256 unless it needs
                                more rounds of workgroups over the 256 CUs than 128 does).
                                Other dtypes: 0 only. */
+  int32_t key_split;        /* FA_KEY_SPLIT_AUTO: with 256-row bf16 items, the work items of a
+                               last round that would leave most CUs idle have their keys split
+                               into parts that run side by side, and a merge kernel combines
+                               the parts' O and LSE (the result is the same attention up to
+                               rounding).  FA_KEY_SPLIT_OFF: never. */
 } fa_layout_desc;
+
+enum { FA_KEY_SPLIT_AUTO = 0, FA_KEY_SPLIT_OFF = 1 };
 
 /* A device tensor [batch][tokens][heads][head_dim], head_dim contiguous. */
 typedef struct {
@@ -201,6 +208,16 @@ fa_status fa_layout_tiles(const fa_layout *L, int32_t *n_tiles, int32_t *block_m
 fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile, fa_range_info *ranges,
                          int32_t cap);
 
+/* Work items whose keys are split (key_split): how many there are and their parts in total.
+ * The tiles above are the block map proper; a split item's parts cover its tile's keys
+ * exactly once between them.  Any pointer may be NULL. */
+fa_status fa_layout_splits(const fa_layout *L, int32_t *n_split, int32_t *n_parts);
+/* Split item s: its tile index, batch*heads + head, its part count, and part p (0 <= p < parts,
+ * or p = -1 for none) with up to cap of its ranges.  FA_ERR_INVALID for an index out of range. */
+fa_status fa_layout_split(const fa_layout *L, int32_t s, int32_t *tile, int32_t *bh,
+                          int32_t *parts, int32_t p, fa_tile_info *part, fa_range_info *ranges,
+                          int32_t cap);
+
 /* Frees a layout (host and device parts).  Work using it must have completed. */
 fa_status fa_layout_destroy(fa_layout *L);
 
@@ -212,6 +229,10 @@ fa_status fa_layout_destroy(fa_layout *L);
  * visible key (impossible under the rule unless T = 0) get O = 0, LSE = -inf.
  * The first call with a layout on a device uploads its block map (unless
  * fa_layout_prepare did); after that it allocates and copies nothing.
+ * A layout with split work items (fa_layout_splits) also gets, with its
+ * block map, a workspace for the parts' partial results (at most 256 slots
+ * of 256*(head_dim+1) floats): calls with one such layout that overlap on a
+ * device (streams without ordering between them) race on it.
  * Asynchronous.
  */
 fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
@@ -220,15 +241,17 @@ fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream)
  * fa_attn_fwd for callers that cannot allocate (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same operation, outputs and checks as
  * fa_attn_fwd, but the layout's block map is copied on every call (one host-to-device copy on
- * `stream`, from the pinned image fa_layout_prepare makes) into a static device array of 4 MiB
- * that the library holds on each GPU until the process ends, and the kernels read it there.
+ * `stream`, from the pinned image fa_layout_prepare makes) into a static device array that
+ * the library holds on each GPU until the process ends, and the kernels read it there.  The
+ * array has 4 MiB for the map and, after it, 32.25 MiB (256 slots of 256*129 floats, the
+ * most any layout asks for) for the partial results of split work items (fa_layout_splits).
  * The call allocates and frees nothing.  L must have been prepared on this device
- * (fa_layout_prepare), else FA_ERR_INVALID.  A block map larger than the array (more than
- * 4 MiB: tiles, ranges and the work list, each part rounded up to 256 bytes) returns
+ * (fa_layout_prepare), else FA_ERR_INVALID.  A block map larger than 4 MiB (tiles, ranges,
+ * the work list and the split items, each part rounded up to 256 bytes) returns
  * FA_ERR_CAPACITY before anything is enqueued.  Every call on a GPU shares that GPU's array,
- * which keeps the last call's map: calls ordered on one stream are safe, calls on different
- * streams of one GPU that may overlap race (one call's copy can overwrite the map another
- * call's kernel is reading).
+ * which keeps the last call's contents: calls ordered on one stream are safe, calls on
+ * different streams of one GPU that may overlap race (one call's copy can overwrite the map
+ * another call's kernel is reading, and their split parts share the workspace).
  */
 fa_status fa_attn_fwd_noalloc(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
 

@@ -112,6 +112,7 @@ class Call:
     v_ref: Optional[np.ndarray] = None
     sink: int = 0  # frames 0 .. sink-1 stay visible (streaming)
     block_rows: int = 0  # bf16 work-item rows (128 or 256); 0 = the library's choice
+    key_split: int = 0   # B.FA_KEY_SPLIT_AUTO or B.FA_KEY_SPLIT_OFF
 
     @property
     def fa_dtype(self):
@@ -122,7 +123,7 @@ class Call:
                            ref_t0=self.ref_t0, chunk_start=self.cs, window=self.window,
                            cache_frames=self.cache, query_rows=self.query_rows,
                            dtype=self.fa_dtype, sink_frames=self.sink,
-                           block_rows=self.block_rows)
+                           block_rows=self.block_rows, key_split=self.key_split)
 
     def problem(self) -> O.Problem:
         z = np.zeros((0, self.H, self.D), np.float32)
@@ -139,7 +140,8 @@ class Call:
 
 
 def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tokens=(),
-                ref_t0=(), query_rows=7, scale_k=1.0, sink=0, block_rows=0) -> Call:
+                ref_t0=(), query_rows=7, scale_k=1.0, sink=0, block_rows=0,
+                key_split=0) -> Call:
     """Seeded N(0,1) inputs (bf16-rounded unless fp32) for one call."""
     g = np.random.default_rng(seed)
 
@@ -151,7 +153,8 @@ def random_call(seed, T, C, H, D, dtype="bf16", cs=0, window=0, cache=0, ref_tok
     lo = 0 if window < 0 else max(0, cs - window)
     c = Call(T=T, C=C, H=H, D=D, dtype=dtype, cs=cs, window=window, cache=cache,
              ref_tokens=list(ref_tokens), ref_t0=list(ref_t0), query_rows=query_rows,
-             hist_first=(0 if sink else lo) if cache else 0, sink=sink, block_rows=block_rows)
+             hist_first=(0 if sink else lo) if cache else 0, sink=sink, block_rows=block_rows,
+             key_split=key_split)
     c.q = {TGT: n(C * T, H, D), SRC: n(C * T, H, D), REF: n(R, H, D)}
     nh = (cs + C - c.hist_first) * T
     c.k_hist, c.v_hist = n(nh, H, D) * scale_k, n(nh, H, D)

@@ -132,24 +132,61 @@ def stream_call(wid, cs, H=None) -> G.Call:
     return c
 
 
-@pytest.mark.parametrize("br", [0, 256], ids=["auto", "bm256"])
-def test_high_res_chunk_full_size_sampled(br):
-    """Full size through the kernel the block map picks (128-row items here) and through the
-    ping-pong kernel."""
+@pytest.mark.parametrize("br,split,n_split", [(0, B.FA_KEY_SPLIT_AUTO, 8),
+                                               (256, B.FA_KEY_SPLIT_OFF, 0),
+                                               (128, B.FA_KEY_SPLIT_AUTO, 0)],
+                         ids=["auto", "bm256_nosplit", "bm128"])
+def test_high_res_chunk_full_size_sampled(br, split, n_split):
+    """Full size through the kernel the block map picks (256-row items with the last round's 8
+    items split into key parts; head 23's last tile is one of them, and the sample holds its
+    rows), through the ping-pong kernel without the split, and through 128-row items."""
     G.say("case: 3600-token chunk at cs=12, window 9, two references (t0 = 0, cs+1), H=24, "
-          "block_rows %d" % br)
+          "block_rows %d, key_split %d" % (br, split))
     c = stream_call(3, 12)
-    c.block_rows = br
+    c.block_rows, c.key_split = br, split
+    L = B.fa_layout_build(c.desc(), c.ring_first)
+    assert B.fa_layout_splits(L)[0] == n_split
+    if n_split:
+        assert 23 in [B.fa_layout_split(L, s)[1] for s in range(n_split)]
     res = G.run_call(c)
     G.compare_sampled(c, res, n_rows=64, heads=[0, 23], what="hi-res chunk")
 
 
 @pytest.mark.parametrize("br", [128, 256], ids=["bm128", "bm256"])
 def test_high_res_chunk_reduced_full_oracle(br):
+    """H = 1: 43 work items of 256 rows, all in one round, so every one is split into key parts
+    (5 each); 128-row items are never split."""
     G.say("case: 3600-token chunk, H=1, every row against the oracle, block_rows %d" % br)
     c = stream_call(3, 12, H=1)
     c.block_rows = br
+    n_split = B.fa_layout_splits(B.fa_layout_build(c.desc(), c.ring_first))[0]
+    assert n_split == (43 if br == 256 else 0)
     G.compare_all(c, G.run_call(c), "hi-res chunk H=1")
+
+
+SPLITS = [
+    # seed, T, C, H, D, cs, window, cache, refs, t0, query_rows, sink
+    (41, 300, 3, 2, 128, 12, 4, 6, [200, 150], [0, 13], 7, 1),  # gate inside the chunk, sink
+    (42, 333, 2, 2, 64, 0, 0, 0, [45], [1], 7, 0),              # bidirectional, ragged frames
+    (43, 520, 3, 3, 128, 9, 6, 9, [], [], 1, 0),                # no reference, ring wraps
+    (44, 77, 5, 1, 128, 0, 0, 0, [500], [2], 3, 0),             # many frames per tile
+]
+
+
+@pytest.mark.parametrize("case", SPLITS, ids=["k%d" % c[0] for c in SPLITS])
+def test_key_split_parts(case):
+    """256-row items whose keys are split into parts (every item of these one-round grids that
+    costs half the largest or more), merged, against the oracle on every row; the same call
+    without the split must agree too."""
+    seed, T, C, H, D, cs, win, cap, refs, t0s, qr, sink = case
+    G.say("case: key split %s" % (case,))
+    c = G.random_call(seed, T, C, H, D, cs=cs, window=win, cache=cap, ref_tokens=refs,
+                      ref_t0=t0s, query_rows=qr, sink=sink, block_rows=256)
+    n_split, n_parts = B.fa_layout_splits(B.fa_layout_build(c.desc(), c.ring_first))
+    assert n_split > 0 and n_parts >= 2 * n_split
+    G.compare_all(c, G.run_call(c), "key split")
+    c.key_split = B.FA_KEY_SPLIT_OFF
+    G.compare_all(c, G.run_call(c), "no key split")
 
 
 # ---------------------------------------------------------------- invariants on the GPU

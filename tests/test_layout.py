@@ -164,14 +164,145 @@ def test_tile_rows_256():
     assert (B.FA_SEG_SRC, 0, 2 * 1560, B.FA_MASK_SAME_FRAME, 0) in ranges
 
 
-@pytest.mark.parametrize("wid,want", [(1, 256), (2, 256), (3, 128)])
-def test_bf16_block_rows_chosen_by_grid(wid, want):
+@pytest.mark.parametrize("wid,split,want,want_splits", [
+    (1, B.FA_KEY_SPLIT_AUTO, 256, (0, 0)), (2, B.FA_KEY_SPLIT_AUTO, 256, (0, 0)),
+    (3, B.FA_KEY_SPLIT_AUTO, 256, (8, 128)), (3, B.FA_KEY_SPLIT_OFF, 128, (0, 0))])
+def test_bf16_block_rows_chosen_by_grid(wid, split, want, want_splits):
     """With block_rows 0 a bf16 layout takes 256-row work items (one 8-wave workgroup per CU)
-    unless they need more rounds over 256 CUs than 128-row items two to a CU: the 1560-token
-    bidirectional call (3156 vs 6300 items: 13 rounds each) and stream chunk (760 vs 1480: 3
-    each) take 256, the 3600-token chunk (1032 vs 2040: 5 vs 4 rounds) 128."""
-    _, bm, _ = B.fa_layout_tiles(workload_layout(wid)[2])
+    unless 128-row items, two to a CU, need clearly fewer rounds over 256 CUs.  The 1560-token
+    bidirectional call (3156 vs 6300 items: 13 rounds each; its last round holds cheap
+    reference rows, not split) and stream chunk (760 vs 1480: 3 rounds each, the last one
+    nearly full) take 256.  The 3600-token chunk has 1032 items = 4 rounds + 8: those 8 are
+    cut into 16 key parts each (128 parts on idle CUs, 1/16 of a round), so 256 rows win over
+    128-row items' 4 rounds; without the key split it is 5 rounds against 4 and takes 128."""
+    w = W.WORKLOADS[wid]
+    cs = w.first_cs
+    if w.streaming:
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.t0_for(cs),
+                        chunk_start=cs, window=w.window, cache_frames=w.cache_frames,
+                        query_rows=B.FA_Q_TARGET, dtype=B.FA_BF16, key_split=split)
+    else:
+        d = B.make_desc(w.C, w.T, w.H, w.D, ref_tokens=w.ref_tokens, ref_t0=w.ref_t0,
+                        query_rows=7, dtype=B.FA_BF16, key_split=split)
+    L = B.fa_layout_build(d)
+    _, bm, _ = B.fa_layout_tiles(L)
     assert bm == want
+    assert B.fa_layout_splits(L) == want_splits
+
+
+def frame_intervals(ranges, fq, T):
+    """Key intervals per segment that the ranges hand to a row of frame fq, masks applied."""
+    out = {}
+    for seg, beg, end, mask, param in ranges:
+        if mask == B.FA_MASK_SAME_FRAME:
+            beg, end = max(beg, fq * T), min(end, (fq + 1) * T)
+        elif mask == B.FA_MASK_GATE and fq < param:
+            continue
+        if beg < end:
+            out.setdefault(seg, []).append((beg, end))
+    return out
+
+
+def merged(iv):
+    """Sorted union of intervals; fails if two of them overlap (a key handed out twice)."""
+    iv = sorted(iv)
+    out = []
+    for b, e in iv:
+        if out:
+            assert b >= out[-1][1], "overlap %s" % ((b, e),)
+        if out and b == out[-1][1]:
+            out[-1] = (out[-1][0], e)
+        else:
+            out.append((b, e))
+    return out
+
+
+def check_splits(L, T, heads):
+    """Every split item's parts: the base tile's rows, ranges inside the base's ranges (same
+    segment, mask and parameter), at least 8 key steps each, and between them every key the base
+    tile hands to each row exactly once (rows of one frame see the same keys, so per frame).
+    Returns (items, parts)."""
+    n_split, n_parts = B.fa_layout_splits(L)
+    n_tiles, bm, bn = B.fa_layout_tiles(L)
+    total = 0
+    seen = set()
+    for s in range(n_split):
+        tile, bh, parts = B.fa_layout_split(L, s)
+        assert 0 <= tile < n_tiles and 0 <= bh < heads and bm == 256
+        assert (tile, bh) not in seen
+        seen.add((tile, bh))
+        assert 2 <= len(parts) <= 16
+        (kind, row0, rows), base = B.fa_layout_tile(L, tile)
+        for (pk, prow0, prows), pr in parts:
+            assert (pk, prow0, prows) == (kind, row0, rows)
+            steps = 0
+            for seg, beg, end, mask, param in pr:
+                assert beg < end
+                assert any(bs == seg and bb <= beg and end <= be and bm_ == mask and bp == param
+                           for bs, bb, be, bm_, bp in base), (seg, beg, end)
+                steps += (end - beg + bn - 1) // bn
+            assert steps >= 8
+        frames = {r // T for r in range(row0, row0 + rows)} if kind < 2 else {0}
+        for fq in frames:
+            want = frame_intervals(base, fq, T)
+            got = {}
+            for _, pr in parts:
+                for seg, iv in frame_intervals(pr, fq, T).items():
+                    got.setdefault(seg, []).extend(iv)
+            assert set(got) == set(want), (tile, fq)
+            for seg in want:
+                assert merged(got[seg]) == merged(want[seg]), (tile, fq, seg)
+        total += len(parts)
+    assert total == n_parts <= 256
+    return n_split, n_parts
+
+
+SPLIT_CASES = [
+    # frames, T, refs, t0, cs, window, cap, query_rows, heads, sink, head_dim
+    (3, 300, [200, 150], [0, 13], 12, 4, 6, 7, 2, 1, 128),   # gate inside the chunk, sink frame
+    (2, 333, [45], [1], 0, 0, 0, 7, 2, 0, 64),               # bidirectional, ragged frames
+    (3, 520, [], [], 9, 6, 9, 1, 3, 0, 128),                  # no reference, ring wraps
+    (5, 77, [500], [2], 0, 0, 0, 3, 1, 0, 128),               # many frames per tile
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(i) for i in range(len(SPLIT_CASES))])
+def test_key_split_parts_cover_tiles(case):
+    F, T, refs, t0s, cs, win, cap, qr, H, sink, hd = case
+    d = B.make_desc(F, T, H, hd, ref_tokens=refs, ref_t0=t0s, chunk_start=cs, window=win,
+                    cache_frames=cap, query_rows=qr, dtype=B.FA_BF16, sink_frames=sink,
+                    block_rows=256)
+    L = B.fa_layout_build(d)
+    n_split, n_parts = check_splits(L, T, H)
+    assert n_split > 0 and n_parts >= 2 * n_split
+    # the split leaves the block map proper and its counts alone
+    d.key_split = B.FA_KEY_SPLIT_OFF
+    L0 = B.fa_layout_build(d)
+    assert B.fa_layout_splits(L0) == (0, 0)
+    assert B.fa_layout_tiles(L0) == B.fa_layout_tiles(L)
+    assert B.fa_layout_stats(L0) == B.fa_layout_stats(L)
+    for i in range(B.fa_layout_tiles(L)[0]):
+        assert B.fa_layout_tile(L0, i) == B.fa_layout_tile(L, i)
+
+
+def test_key_split_workload_parts():
+    """The 3600-token chunk's 8 split items: 16 parts each, one split per (tile, head)."""
+    w, d, L = workload_layout(3)
+    assert check_splits(L, w.T, w.H) == (8, 128)
+
+
+def test_key_split_not_for_128_rows_or_cheap_items():
+    # 128-row items: never split
+    d = B.make_desc(3, 300, 2, 128, ref_tokens=[200], ref_t0=[0], chunk_start=12, window=4,
+                    cache_frames=6, dtype=B.FA_BF16, block_rows=128)
+    assert B.fa_layout_splits(B.fa_layout_build(d)) == (0, 0)
+    # items under 16 key steps (1024 keys): not worth a split
+    d = B.make_desc(2, 150, 2, 128, ref_tokens=[100], ref_t0=[0], query_rows=7, block_rows=256)
+    assert B.fa_layout_splits(B.fa_layout_build(d)) == (0, 0)
+    # a bad key_split value
+    d.key_split = 2
+    with pytest.raises(B.FaError):
+        B.fa_layout_build(d)
 
 
 def workload_layout(wid, cs=None):

@@ -1,7 +1,9 @@
 """fa_attn_fwd_noalloc (the allocation-free attention call) against fa_attn_fwd through the C
-ABI: outputs bit-identical, and within the bf16 tolerance of the oracle, on two calls in a row
-on one stream -- a 40-head streaming chunk, then a smaller bidirectional call with every query
-kind -- plus the host-side errors (unprepared layout, block map beyond the static array)."""
+ABI: outputs bit-identical, and within the bf16 tolerance of the oracle, on calls in a row on
+one stream -- a 40-head streaming chunk whose 120 items are split into key parts (the parts'
+workspace lives in the static array), a smaller bidirectional call with every query kind, and
+a smaller split call that reuses the workspace -- plus the host-side errors (unprepared layout,
+block map beyond the static array)."""
 import ctypes
 
 import numpy as np
@@ -67,15 +69,20 @@ def _run(c, noalloc):
 @pytest.mark.gpu
 def test_noalloc_matches_fa_attn_fwd_two_calls():
     calls = [
-        ("40-head streaming chunk (T=200, ring wraps, gated reference), ping-pong kernel",
+        ("40-head streaming chunk (T=200, ring wraps, gated reference), ping-pong kernel, "
+         "120 items in 2 key parts each",
          G.random_call(71, 200, 3, 40, 128, "bf16", cs=9, window=6, cache=7, ref_tokens=[64, 40],
-                       ref_t0=[0, 10], query_rows=1, block_rows=256)),
+                       ref_t0=[0, 10], query_rows=1, block_rows=256), 120),
         ("smaller bidirectional call (T=40, F=3, H=2, every query kind), 4-wave kernel",
          G.random_call(72, 40, 3, 2, 128, "bf16", ref_tokens=[24], ref_t0=[1], query_rows=7,
-                       block_rows=128)),
+                       block_rows=128), 0),
+        ("smaller split call (T=300, F=2, H=1, head_dim 64), ping-pong kernel",
+         G.random_call(73, 300, 2, 1, 64, "bf16", ref_tokens=[100], ref_t0=[1], query_rows=3,
+                       block_rows=256), 2),
     ]
-    for what, c in calls:
+    for what, c, n_split in calls:
         G.say("case: %s" % what)
+        assert B.fa_layout_splits(B.fa_layout_build(c.desc(), c.ring_first))[0] == n_split
         want = _run(c, noalloc=False)
         got = _run(c, noalloc=True)
         assert want.keys() == got.keys()
