@@ -465,6 +465,28 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 //     operands, so every row of L holds the 16 queries' sums and lane l reads
 //     its query's in place.  The softmax phase, which sets the pace, then has no
 //     row-sum arithmetic; the matrix phase has room for the four extra MFMAs.
+// max(a, b) for values that are never NaN, without the quieting of signalling NaNs an IEEE-mode
+// v_max_f32 asks of inputs it cannot prove canonical (lane exchanges and pinned MFMA results):
+// the middle of (a, b, +inf) is the larger of a and b, -inf included.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+}
+
+// Row maxima of both 16-row query blocks across the four lanes of a query (l16 + {0, 16, 32,
+// 48}), given each lane's partial maxima m0 (block 0) and m1 (block 1).  The first exchange
+// swaps m0 of lanes 32-63 with m1 of lanes 0-31, so one max leaves block 0's half-reduced value
+// in lanes 0-31 and block 1's in lanes 32-63; one 16-lane exchange finishes each, and a last
+// 32-lane exchange hands every lane both blocks' maxima.
+__device__ __forceinline__ void rows_max2(float &m0, float &m1) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+  float h = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(h), __float_as_uint(h), false, false);
+  h = max_nn(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+  auto r3 = __builtin_amdgcn_permlane32_swap(__float_as_uint(h), __float_as_uint(h), false, false);
+  m0 = __uint_as_float(r3[0]);
+  m1 = __uint_as_float(r3[1]);
+}
+
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) {
   using Cfg = Bf16Cfg<D>;
@@ -610,6 +632,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   const bf16x8_t ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                           (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   const float c = a.c;
+  const float cinv = 1.0f / a.c;
   f32x4_t s[4][2];  // S^T of the tile awaiting its softmax, [kb][qb]
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4_t{};
@@ -724,24 +747,30 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
             }
         }
       }
+      // row max: in-lane over the 16 scores of each query block as three-way maxima, then
+      // across the four lanes that share the query (l16 + {0, 16, 32, 48}), both blocks at once
+      float rmax[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        // row max: in-lane over the 16 scores as three-way maxima, then across the four lanes
-        // that share the query (l16 + {0, 16, 32, 48})
         const float m0 = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
         const float m1 = fmaxf(fmaxf(s[0][qb][3], s[1][qb][0]), s[1][qb][1]);
         const float m2 = fmaxf(fmaxf(s[1][qb][2], s[1][qb][3]), s[2][qb][0]);
         const float m3 = fmaxf(fmaxf(s[2][qb][1], s[2][qb][2]), s[2][qb][3]);
         const float m4 = fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), s[3][qb][2]);
-        float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
-        mx = xhalf_max(mx);
-        mx = x16_max(mx);
-        // lazy max update: raised only past m_run + 8 (values stay <= 2^8)
-        const float mt = mx * c;
-        const bool need = mt > m_run[qb] + kThr;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
-        m_run[qb] = need ? mt : m_run[qb];
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        rmax[qb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
+      }
+      rows_max2(rmax[0], rmax[1]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mx = rmax[qb];
+        // lazy max update: raised only when a row's max passes m_run + 8 (values stay <= 2^8),
+        // tested on the raw scores against (m_run + 8) / c; the update and the O rescale sit
+        // in the rare branch
+        const bool need = mx > fmaf(m_run[qb], cinv, kThr * cinv);
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float mt = mx * c;
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
+          m_run[qb] = need ? mt : m_run[qb];
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= alpha;
           lsum[qb] *= alpha;
