@@ -439,14 +439,16 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs a) {
 }
 
 // Ping-pong kernel.  Waves 0-3 (group A) and 4-7 (group B) share the four
-// SIMDs, one of each per SIMD (waves are dealt to SIMDs round robin).  Time
-// is cut into slots by workgroup barriers: in every slot one group runs its
-// matrix phase (S of the next tile and O += V P of this one: MFMAs and LDS
-// reads only) while the other runs its softmax phase (VALU only), and the
-// roles swap at the barrier, so each SIMD's matrix core is fed by one wave
-// while the other wave's exp work issues beside it.  Group A also issues the
-// direct loads of the pair's K and V tiles, one every few MFMAs of its matrix
-// phase; they have the pair's second slot to land.
+// SIMDs, one of each per SIMD (waves are dealt to SIMDs round robin).  Each
+// key tile is a pair of phases per wave: group A runs its matrix phase (S of
+// the next tile and O += V P of this one: MFMAs and LDS reads only) and then
+// its softmax phase (VALU only), group B the other way round, so each SIMD's
+// matrix core is fed by one wave while the other wave's exp work issues beside
+// it.  One workgroup barrier per tile publishes the next tiles' direct loads;
+// between two of them the waves of a SIMD swap roles on their own (a barrier
+// at the swap, holding all four SIMDs in step, made the kernel 2-3% slower).
+// Group A issues the direct loads of the pair's K and V tiles at the start of
+// its matrix phase; they have the whole pair to land.
 //
 // Its products run on v_mfma_f32_16x16x32_bf16 (16x16 outputs, 32-deep), which
 // sustains a higher share of the matrix core's peak on gfx950 than the 32x32x16
@@ -510,7 +512,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   const int tid = threadIdx.x;
   // the wave index is uniform per wave; say so, since it feeds M0 (LDS address of direct loads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grp_a = wave < 4;  // group A: matrix phase first in every slot pair
+  const bool grp_a = wave < 4;  // group A: matrix phase first in every pair
   const int lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int T = a.T;
   // a wave whose 32 rows all lie past the tile's end only loads and keeps step
@@ -794,14 +796,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     next(cc, 0);
   };
 
-  // Slot ends.  The first barrier of a slot pair only hands the phases over (no data is
-  // published: the buffers read on both sides of it were filled before the pair began), so it
-  // waits for nothing.  The second one publishes the pair's direct loads: every wave waits for
-  // its own, then the barrier (its fence also completes every LDS read of the pair, freeing
-  // those buffers for the next pair's loads).
-  // A phase's results are pinned before the barrier that ends it: the instruction selector
+  // Phase ends.  Between the two phases of a pair no data changes hands (the buffers both
+  // phases read were filled before the pair began), so the swap is only a scheduling fence.
+  // The pair's end publishes its direct loads: every wave waits for its own, then the barrier
+  // (its fence also completes every LDS read of the pair, freeing those buffers for the next
+  // pair's loads).
+  // A phase's results are pinned before the fence that ends it: the instruction selector
   // orders only side-effecting nodes, so without the pins it may place pure arithmetic of one
-  // phase after the barrier, in the next.
+  // phase after the fence, in the next.
   auto pin_softmax = [&]() {
 #pragma unroll
     for (int t = 0; t < 2; ++t) __asm__ volatile("" : "+v"(pw[t][0]), "+v"(pw[t][1]));
@@ -814,12 +816,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     for (int cb = 0; cb < CB; ++cb) __asm__ volatile("" : "+v"(oacc[cb][0]), "+v"(oacc[cb][1]));
     __asm__ volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));
   };
-  // Neither barrier may have arithmetic moved across it (the machine scheduler would otherwise
-  // pull the exp work of a softmax phase into the neighbouring matrix phase).
+  // No arithmetic may be moved across a phase end (the machine scheduler would otherwise pull
+  // the exp work of a softmax phase into the neighbouring matrix phase).
   auto handover = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -839,7 +839,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     k1c = k0c;
     next(k1c, 1);
     // prologue: K_0 -> kbuf0, V_0 -> vbuf0, K_1 -> kbuf1; S_0 everywhere, softmax of S_0 in
-    // group A (group B takes it in the first slot)
+    // group A (group B takes it in the first pair)
     if (grp_a) {
       issue(k0c, false, kbuf0);
       issue(cv, true, vbuf0);
@@ -857,7 +857,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
-    // Slot pair j: loads of K_{j+2} and V_{j+1} (by group A, during its matrix phase); the
+    // Pair j: loads of K_{j+2} and V_{j+1} (by group A, at its matrix phase); the
     // matrix phase reads K_{j+1} and V_j.  Even pairs read kbuf1 / vbuf0 and load into kbuf0 /
     // vbuf1, odd pairs the other way round; unrolled by two so the buffers are compile-time
     // names.  Group A, group B and the waves without rows run separate copies of the loop
