@@ -4,7 +4,9 @@ append), replayed against eager execution of the same chunks: bit-identical outp
 A ring of 12 frames and 3-frame chunks repeat their slot pattern every 4 chunks, and once the
 ring is full every steady chunk has the same block map; so one graph per phase (captured at
 chunks 4..7) replays chunks 4..13.  Between replays the test does its own eager work (copying the
-next chunk's inputs into the static buffers) and synchronises, and checks every replay."""
+next chunk's inputs into the static buffers) and synchronises, and checks every replay.  At two
+heads the bf16 chunk's 38 work items of 256 rows fit one round, so they are split into key parts
+and each bf16 graph also holds the merge kernel."""
 import pytest
 import torch
 
@@ -116,6 +118,7 @@ def test_graph_replay_matches_eager(lowbit):
             L = graph.layout(cs)
             if captured_map is None:
                 captured_map = block_map(L)
+                assert (B.fa_layout_splits(L)[0] == 0) == lowbit, "bf16 items split into parts"
             assert block_map(L) == captured_map, "steady chunks share one block map"
             phase = ch % 4
             if phase not in graphs:
