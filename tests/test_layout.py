@@ -285,6 +285,45 @@ def test_key_split_parts_cover_tiles(case):
         assert B.fa_layout_tile(L0, i) == B.fa_layout_tile(L, i)
 
 
+def test_key_split_random_layouts():
+    """Seeded random bf16 geometries (streaming or bidirectional, references with gates, sink
+    frames, all query kinds, 256-row items): wherever the layout splits items, the parts keep
+    the invariants of check_splits; the block map proper is the one of the unsplit layout."""
+    g = np.random.default_rng(2024)
+    split_seen = 0
+    for _ in range(60):
+        F = int(g.integers(1, 6))
+        T = int(g.integers(1, 700))
+        nref = int(g.integers(0, 3))
+        refs = [int(g.integers(0, 600)) for _ in range(nref)]
+        H = int(g.integers(1, 9))
+        qr = int(g.integers(1, 8))
+        if g.random() < 0.5:
+            cs, win, cap, sink = 0, 0, 0, 0
+        else:
+            sink = int(g.integers(0, 3))
+            win = int(g.integers(0, 10))
+            cap = win + sink + int(g.integers(0, 3))
+            cs = int(g.integers(0, 20))
+            if cap == 0:
+                cap = 1
+        t0s = [int(g.integers(0, cs + F + 2)) for _ in range(nref)]
+        d = B.make_desc(F, T, H, 128, ref_tokens=refs, ref_t0=t0s, chunk_start=cs, window=win,
+                        cache_frames=cap, query_rows=qr, dtype=B.FA_BF16, sink_frames=sink,
+                        block_rows=256)
+        try:
+            L = B.fa_layout_build(d)
+        except B.FaError:
+            continue  # a geometry the ring cannot hold
+        n_split, _ = check_splits(L, T, H)
+        split_seen += n_split > 0
+        d.key_split = B.FA_KEY_SPLIT_OFF
+        L0 = B.fa_layout_build(d)
+        assert B.fa_layout_tiles(L0) == B.fa_layout_tiles(L)
+        assert B.fa_layout_stats(L0) == B.fa_layout_stats(L)
+    assert split_seen >= 10
+
+
 def test_key_split_workload_parts():
     """The 3600-token chunk's 8 split items: 16 parts each, one split per (tile, head)."""
     w, d, L = workload_layout(3)
