@@ -42,7 +42,7 @@ class fa_tensor(C.Structure):
 
 _IO_TENSORS = ["q_tgt", "q_src", "q_ref", "k_ring", "v_ring", "k_tgt", "v_tgt", "k_src", "v_src",
                "k_ref", "v_ref", "o_tgt", "o_src", "o_ref"]
-_IO_PTRS = ["lse_tgt", "lse_src", "lse_ref", "k_mean", "v_absmax"]
+_IO_PTRS = ["lse_tgt", "lse_src", "lse_ref", "k_mean", "v_absmax", "workspace"]
 
 
 class fa_io(C.Structure):
@@ -87,6 +87,7 @@ def _load():
         "fa_layout_tiles": ([P] + [C.POINTER(C.c_int32)] * 3, C.c_int),
         "fa_layout_tile": ([P, C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
                             C.c_int32], C.c_int),
+        "fa_layout_workspace_bytes": ([P, C.POINTER(C.c_size_t)], C.c_int),
         "fa_layout_splits": ([P, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
         "fa_layout_split": ([P, C.c_int32] + [C.POINTER(C.c_int32)] * 3 +
                             [C.c_int32, C.POINTER(fa_tile_info), C.POINTER(fa_range_info),
@@ -237,6 +238,13 @@ def fa_layout_tile(L: Layout, i: int):
     _check(lib.fa_layout_tile(L.handle, i, C.byref(t), rr, 64), "fa_layout_tile")
     ranges = [(r.seg, r.begin, r.end, r.mask, r.param) for r in rr[:t.n_ranges]]
     return (t.q_kind, t.row0, t.rows), ranges
+
+
+def fa_layout_workspace_bytes(L: Layout) -> int:
+    """Bytes of key-split scratch a call with L needs (fa_io.workspace); 0 if nothing is split."""
+    n = C.c_size_t()
+    _check(lib.fa_layout_workspace_bytes(L.handle, C.byref(n)), "fa_layout_workspace_bytes")
+    return n.value
 
 
 def fa_layout_splits(L: Layout):

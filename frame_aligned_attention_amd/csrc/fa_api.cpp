@@ -121,9 +121,11 @@ fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
   a.tiles = m.tiles;
   a.ranges = m.ranges;
   a.work = m.work;
-  a.ws = m.ws;
+  a.ws = io->workspace ? (float *)io->workspace : m.ws;
   a.splits = m.splits;
-  if (!L->splits.empty() && !m.ws) return fail(FA_ERR_INVALID, "split layout without a workspace");
+  if (io->workspace && ((uintptr_t)io->workspace) % 16)
+    return fail(FA_ERR_INVALID, "workspace not 16-byte aligned");
+  if (!L->splits.empty() && !a.ws) return fail(FA_ERR_INVALID, "split layout without a workspace");
   const int grid = (int)L->work.size();
   hipError_t e;
   if (d.dtype == FA_F32)

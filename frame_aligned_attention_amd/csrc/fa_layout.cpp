@@ -542,6 +542,13 @@ extern "C" fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info 
   return FA_OK;
 }
 
+extern "C" fa_status fa_layout_workspace_bytes(const fa_layout *L, size_t *bytes) {
+  if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
+  if (!bytes) return fail(FA_ERR_INVALID, "bytes is NULL");
+  *bytes = ws_bytes(L);
+  return FA_OK;
+}
+
 extern "C" fa_status fa_layout_splits(const fa_layout *L, int32_t *n_split, int32_t *n_parts) {
   if (!L) return fail(FA_ERR_INVALID, "layout is NULL");
   if (n_split) *n_split = (int32_t)L->splits.size();

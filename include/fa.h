@@ -39,6 +39,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -133,6 +134,10 @@ typedef struct {
   float *k_mean;   /* FA_LOWBIT quantiser: per-head channel mean [batch][heads][head_dim] */
   float *v_absmax; /* FA_LOWBIT quantiser, optional (NULL = not kept): largest V block
                       scale of the call [batch][heads]; fa_attn_fwd does not read it */
+  void *workspace; /* optional: device scratch for the partial results of key-split work
+                      items (fa_layout_splits), fa_layout_workspace_bytes(L) bytes, 16-byte
+                      aligned, used by no other call while this one runs; NULL = the layout's
+                      own (calls with one layout that overlap on a device then race on it) */
 } fa_io;
 
 typedef struct fa_layout fa_layout; /* opaque, immutable after build */
@@ -208,6 +213,9 @@ fa_status fa_layout_tiles(const fa_layout *L, int32_t *n_tiles, int32_t *block_m
 fa_status fa_layout_tile(const fa_layout *L, int32_t i, fa_tile_info *tile, fa_range_info *ranges,
                          int32_t cap);
 
+/* Bytes of key-split scratch a call with L needs (0 when nothing is split): what
+ * fa_io.workspace must provide.  FA_ERR_INVALID if L or bytes is NULL. */
+fa_status fa_layout_workspace_bytes(const fa_layout *L, size_t *bytes);
 /* Work items whose keys are split (key_split): how many there are and their parts in total.
  * The tiles above are the block map proper; a split item's parts cover its tile's keys
  * exactly once between them.  Any pointer may be NULL. */
@@ -231,8 +239,10 @@ fa_status fa_layout_destroy(fa_layout *L);
  * fa_layout_prepare did); after that it allocates and copies nothing.
  * A layout with split work items (fa_layout_splits) also gets, with its
  * block map, a workspace for the parts' partial results (at most 256 slots
- * of 256*(head_dim+1) floats): calls with one such layout that overlap on a
- * device (streams without ordering between them) race on it.
+ * of 256*(head_dim+1) floats); io->workspace, when given, is used instead.
+ * Calls with one such layout that overlap on a device (streams without
+ * ordering between them) must each bring their own io->workspace, else they
+ * race on the layout's.  FA_ERR_INVALID for a misaligned workspace.
  * Asynchronous.
  */
 fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream);
@@ -244,7 +254,8 @@ fa_status fa_attn_fwd(const fa_layout *L, const fa_io *io, fa_hip_stream stream)
  * `stream`, from the pinned image fa_layout_prepare makes) into a static device array that
  * the library holds on each GPU until the process ends, and the kernels read it there.  The
  * array has 4 MiB for the map and, after it, 32.25 MiB (256 slots of 256*129 floats, the
- * most any layout asks for) for the partial results of split work items (fa_layout_splits).
+ * most any layout asks for) for the partial results of split work items (fa_layout_splits),
+ * unless io->workspace brings the caller's.
  * The call allocates and frees nothing.  L must have been prepared on this device
  * (fa_layout_prepare), else FA_ERR_INVALID.  A block map larger than 4 MiB (tiles, ranges,
  * the work list and the split items, each part rounded up to 256 bytes) returns

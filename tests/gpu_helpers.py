@@ -184,8 +184,9 @@ def ring_tensors(c: Call, tdtype, poison=None):
     return dev(kr, tdtype), dev(vr, tdtype)
 
 
-def run_call(c: Call, poison=None, out_fill=None, layout=None, stream=None):
-    """Runs fa_attn_fwd for the call; returns {kind: (O [rows,H,D] fp32, LSE [H,rows])}."""
+def run_call(c: Call, poison=None, out_fill=None, layout=None, stream=None, workspace=None):
+    """Runs fa_attn_fwd for the call; returns {kind: (O [rows,H,D] fp32, LSE [H,rows])}.
+    workspace: a device tensor for fa_io.workspace (None: the layout's own)."""
     tdt = torch.float32 if c.dtype == "f32" else torch.bfloat16
     t = {}
     if TGT in c.kinds():
@@ -215,6 +216,8 @@ def run_call(c: Call, poison=None, out_fill=None, layout=None, stream=None):
         t["lse_" + nm] = torch.full((1, c.H, rows[k]), fill, dtype=torch.float32, device="cuda")
         outs[k] = nm
     L = layout or B.fa_layout_build(c.desc(), c.ring_first)
+    if workspace is not None:
+        t["workspace"] = workspace
     io = B.make_io(t)
     B.fa_attn_fwd(L, io, stream)
     torch.cuda.synchronize()

@@ -176,15 +176,25 @@ SPLITS = [
 @pytest.mark.parametrize("case", SPLITS, ids=["k%d" % c[0] for c in SPLITS])
 def test_key_split_parts(case):
     """256-row items whose keys are split into parts (every item of these one-round grids that
-    costs half the largest or more), merged, against the oracle on every row; the same call
-    without the split must agree too."""
+    costs half the largest or more), merged, against the oracle on every row; with a workspace
+    of the caller's the output is bit-identical; the same call without the split must agree
+    with the oracle too."""
     seed, T, C, H, D, cs, win, cap, refs, t0s, qr, sink = case
     G.say("case: key split %s" % (case,))
     c = G.random_call(seed, T, C, H, D, cs=cs, window=win, cache=cap, ref_tokens=refs,
                       ref_t0=t0s, query_rows=qr, sink=sink, block_rows=256)
-    n_split, n_parts = B.fa_layout_splits(B.fa_layout_build(c.desc(), c.ring_first))
+    L = B.fa_layout_build(c.desc(), c.ring_first)
+    n_split, n_parts = B.fa_layout_splits(L)
     assert n_split > 0 and n_parts >= 2 * n_split
-    G.compare_all(c, G.run_call(c), "key split")
+    res = G.run_call(c, layout=L)
+    G.compare_all(c, res, "key split")
+    # the same call with a workspace of the caller's (fa_io.workspace): bit-identical
+    nbytes = B.fa_layout_workspace_bytes(L)
+    assert nbytes == n_parts * 256 * (D + 1) * 4
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    res_ws = G.run_call(c, layout=L, workspace=ws)
+    for k in res:
+        assert np.array_equal(res_ws[k][0], res[k][0]) and np.array_equal(res_ws[k][1], res[k][1])
     c.key_split = B.FA_KEY_SPLIT_OFF
     G.compare_all(c, G.run_call(c), "no key split")
 

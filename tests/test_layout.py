@@ -325,9 +325,12 @@ def test_key_split_random_layouts():
 
 
 def test_key_split_workload_parts():
-    """The 3600-token chunk's 8 split items: 16 parts each, one split per (tile, head)."""
+    """The 3600-token chunk's 8 split items: 16 parts each, one split per (tile, head); their
+    scratch is 128 slots of 256 x 129 floats."""
     w, d, L = workload_layout(3)
     assert check_splits(L, w.T, w.H) == (8, 128)
+    assert B.fa_layout_workspace_bytes(L) == 128 * 256 * 129 * 4
+    assert B.fa_layout_workspace_bytes(workload_layout(2)[2]) == 0
 
 
 def test_key_split_not_for_128_rows_or_cheap_items():
