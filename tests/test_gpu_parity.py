@@ -199,6 +199,39 @@ def test_key_split_parts(case):
     G.compare_all(c, G.run_call(c), "no key split")
 
 
+def test_key_split_batch2():
+    """Batch 2 with split work items (the merge takes batch and head from the item's
+    batch*heads index): each batch entry against its own oracle, every row."""
+    G.say("case: key split, batch 2 (T=300, C=3, H=2, gated reference)")
+    T, C, H, D = 300, 3, 2, 128
+    calls = [G.random_call(60 + b, T, C, H, D, "bf16", ref_tokens=[200], ref_t0=[1],
+                           query_rows=7, block_rows=256) for b in range(2)]
+    d = B.make_desc(C, T, H, D, batch=2, ref_tokens=[200], ref_t0=[1], query_rows=7,
+                    block_rows=256)
+    L = B.fa_layout_build(d)
+    n_split, _ = B.fa_layout_splits(L)
+    assert n_split > 0
+    assert {B.fa_layout_split(L, s)[1] // H for s in range(n_split)} == {0, 1}  # both batches
+    bf = lambda xs: torch.from_numpy(np.stack(xs)).to("cuda").to(torch.bfloat16).contiguous()
+    t = {}
+    for name, src in (("tgt", lambda c: (c.q[TGT], c.k_hist, c.v_hist)),
+                      ("src", lambda c: (c.q[SRC], c.k_src, c.v_src)),
+                      ("ref", lambda c: (c.q[REF], c.k_ref, c.v_ref))):
+        qs, ks, vs = zip(*[src(c) for c in calls])
+        t["q_" + name], t["k_" + name], t["v_" + name] = bf(qs), bf(ks), bf(vs)
+        rows = t["q_" + name].shape[1]
+        t["o_" + name] = torch.full((2, rows, H, D), float("nan"), dtype=torch.bfloat16,
+                                    device="cuda")
+        t["lse_" + name] = torch.full((2, H, rows), float("nan"), dtype=torch.float32,
+                                      device="cuda")
+    B.fa_attn_fwd(L, B.make_io(t))
+    torch.cuda.synchronize()
+    for b, c in enumerate(calls):
+        res = {k: (G.host(t["o_" + nm][b]), G.host(t["lse_" + nm][b]))
+               for k, nm in ((TGT, "tgt"), (SRC, "src"), (REF, "ref"))}
+        G.compare_all(c, res, "key split batch %d" % b)
+
+
 # ---------------------------------------------------------------- invariants on the GPU
 
 def test_source_perturbation_is_local():
