@@ -457,10 +457,12 @@ __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x1[i]);
     mx = xhalf_max(mx);
     const float mt = (mx - kBias) * fk;  // the difference is exact; fk > 0; -inf stays -inf
+    // the new max, the exp of alpha and the rescale only in the branch, taken when some row's
+    // max grew
     const bool need = mt > m_run + kThr;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-    m_run = need ? mt : m_run;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+      m_run = need ? mt : m_run;
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
       // lanes 0-15 hold the sums of queries l and l + 16: the latter's alpha from lane l + 16
