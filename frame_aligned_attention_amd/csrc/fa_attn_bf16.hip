@@ -701,10 +701,11 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
       for (int cb = 0; cb < CB; ++cb) pv_step(Vl, t, cb);
     rowsum_step(0);
     rowsum_step(1);
-    // operands six MFMA pairs ahead (~190 cycles of matrix work, the LDS latency under this
+    // operands five MFMA pairs ahead (~160 cycles of matrix work, the LDS latency under this
     // load): K reads (one per QK pair), then V reads (two per PV pair).  Three pairs ahead was
-    // 2-3% slower; seven leaves too few registers beside the row-sum accumulators.
-    constexpr int LA = 6;
+    // 2-3% slower, six level; seven and more leave too few registers, and more reads in flight
+    // only add LDS contention.
+    constexpr int LA = 5;
     __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS read: K operands of pairs 0..LA-1
 #pragma unroll
     for (int i = 0; i < NQK + NPV + 2; ++i) {
@@ -762,21 +763,27 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
         rmax[qb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
       }
       rows_max2(rmax[0], rmax[1]);
+      // lazy max update: raised only when a row's max passes m_run + 8 (values stay <= 2^8),
+      // tested on the raw scores against (m_run + 8) / c; the update and the O rescale of both
+      // query blocks sit in one rare branch
+      {
+        const bool need0 = rmax[0] > fmaf(m_run[0], cinv, kThr * cinv);
+        const bool need1 = rmax[1] > fmaf(m_run[1], cinv, kThr * cinv);
+        if (__builtin_amdgcn_ballot_w64(need0 || need1) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const bool need = qb == 0 ? need0 : need1;
+            const float mt = rmax[qb] * c;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
+            m_run[qb] = need ? mt : m_run[qb];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= alpha;
+            lsum[qb] *= alpha;
+          }
+        }
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float mx = rmax[qb];
-        // lazy max update: raised only when a row's max passes m_run + 8 (values stay <= 2^8),
-        // tested on the raw scores against (m_run + 8) / c; the update and the O rescale sit
-        // in the rare branch
-        const bool need = mx > fmaf(m_run[qb], cinv, kThr * cinv);
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float mt = mx * c;
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.0f;
-          m_run[qb] = need ? mt : m_run[qb];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[cb][qb] *= alpha;
-          lsum[qb] *= alpha;
-        }
         const float mneg = -m_run[qb];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
