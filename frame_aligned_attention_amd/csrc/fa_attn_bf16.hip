@@ -673,13 +673,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // pw).  After the last tile the S product runs on whatever `kbuf` holds and is dropped: one
   // straight-line block, so the accumulators keep their registers.  Operand reads run a few
   // MFMAs ahead.  In group A the phase also issues the pair's direct loads (K at cursor ck
-  // into `kw`, V at cursor cv into `vw`), one every few MFMAs, so they trickle into the
-  // load path instead of queueing behind each other.
+  // into `kw`, V at cursor cv into `vw`), one per MFMA pair over the phase's last pairs (the
+  // PV products, whose operand reads are behind them by then): spread over the whole phase
+  // they competed with its K reads and were 0.4-1.8% slower.
   auto matrix_phase = [&](const char *kbuf, const char *vbuf, auto with_loads, const Cur &kc,
                           char *kw, const Cur &vc, char *vw) {
     const lds_char *Kl = (const lds_char *)kbuf, *Vl = (const lds_char *)vbuf;
     constexpr int NQK = 4 * KS, NPV = 2 * CB, NL = 2 * Cfg::LOADS;  // in pairs of MFMAs
-    constexpr int EVERY = (NQK + NPV) / NL;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4_t{};
     if constexpr (decltype(with_loads)::value) {
@@ -711,7 +711,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     for (int i = 0; i < NQK + NPV + 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA pair (QK, then PV, then sums)
       if constexpr (decltype(with_loads)::value)
-        if (i % EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+        if (i >= NQK + NPV + 2 - NL)  // the loads, one per pair of the last NL pairs
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       if (i + LA < NQK)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       else if (i + LA < NQK + NPV)
