@@ -46,7 +46,8 @@ _IO_PTRS = ["lse_tgt", "lse_src", "lse_ref", "k_mean", "v_absmax", "workspace"]
 
 
 class fa_io(C.Structure):
-    _fields_ = [(n, fa_tensor) for n in _IO_TENSORS] + [(n, C.c_void_p) for n in _IO_PTRS]
+    _fields_ = ([(n, fa_tensor) for n in _IO_TENSORS] + [(n, C.c_void_p) for n in _IO_PTRS] +
+                [("workspace_bytes", C.c_size_t)])
 
 
 class fa_tile_info(C.Structure):
@@ -195,6 +196,9 @@ def make_io(tensors: Dict[str, object], scales: Optional[Dict[str, object]] = No
     for n in _IO_PTRS:
         if tensors.get(n) is not None:
             setattr(io, n, tensors[n].data_ptr())
+    if tensors.get("workspace") is not None:
+        ws = tensors["workspace"]
+        io.workspace_bytes = ws.numel() * ws.element_size()
     return io
 
 

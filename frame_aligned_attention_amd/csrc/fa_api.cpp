@@ -125,6 +125,9 @@ fa_status attn_fwd_map(const fa_layout *L, const fa_io *io, hipStream_t stream,
   a.splits = m.splits;
   if (io->workspace && ((uintptr_t)io->workspace) % 16)
     return fail(FA_ERR_INVALID, "workspace not 16-byte aligned");
+  if (io->workspace && io->workspace_bytes < ws_bytes(L))
+    return fail(FA_ERR_INVALID, "workspace of " + std::to_string(io->workspace_bytes) +
+                                    " bytes; the layout needs " + std::to_string(ws_bytes(L)));
   if (!L->splits.empty() && !a.ws) return fail(FA_ERR_INVALID, "split layout without a workspace");
   const int grid = (int)L->work.size();
   hipError_t e;

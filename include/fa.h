@@ -135,9 +135,11 @@ typedef struct {
   float *v_absmax; /* FA_LOWBIT quantiser, optional (NULL = not kept): largest V block
                       scale of the call [batch][heads]; fa_attn_fwd does not read it */
   void *workspace; /* optional: device scratch for the partial results of key-split work
-                      items (fa_layout_splits), fa_layout_workspace_bytes(L) bytes, 16-byte
-                      aligned, used by no other call while this one runs; NULL = the layout's
-                      own (calls with one layout that overlap on a device then race on it) */
+                      items (fa_layout_splits), at least fa_layout_workspace_bytes(L) bytes,
+                      16-byte aligned, used by no other call while this one runs; NULL = the
+                      layout's own (calls with one layout that overlap on a device then race
+                      on it) */
+  size_t workspace_bytes; /* size of workspace; a smaller one than L needs is FA_ERR_INVALID */
 } fa_io;
 
 typedef struct fa_layout fa_layout; /* opaque, immutable after build */

@@ -195,6 +195,9 @@ def test_key_split_parts(case):
     res_ws = G.run_call(c, layout=L, workspace=ws)
     for k in res:
         assert np.array_equal(res_ws[k][0], res[k][0]) and np.array_equal(res_ws[k][1], res[k][1])
+    with pytest.raises(B.FaError) as err:  # 4 bytes short: refused before any launch
+        G.run_call(c, layout=L, workspace=ws[: (nbytes - 4) // 4])
+    assert err.value.status == B.FA_ERR_INVALID
     c.key_split = B.FA_KEY_SPLIT_OFF
     G.compare_all(c, G.run_call(c), "no key split")
 
