@@ -279,8 +279,10 @@ __global__ void __launch_bounds__(512, 1) w8a8_gemm_kernel(const W8GemmArgs a) {
   // dequantises block kb-1; in the second, A dequantises kb while B multiplies it.  A barrier
   // (no fence) hands the slots over; the step's last barrier publishes block kb+1.  Each group
   // keeps one set of int32 products; A's live within a step, B's across the publish.
-  // At the start of a step every wave issues the scales of its block and its share of the tiles
-  // of block kb+2 (scales first, so that waiting for them leaves the tile loads in flight).  At
+  // At the start of a step every wave issues the scales of its block; its share of the tiles of
+  // block kb+2 follows once its MFMAs of the step are issued (group A: after its MFMA slot,
+  // group B: after the publish), so the direct loads' LDS writes do not meet the operand reads
+  // of the MFMA slots (loads at the start of A's step were 2% slower).  At
   // the step's end each wave waits for all but the newest six loads (block kb+1 has landed).  The
   // waits are s_waitcnt builtins, which the compiler's own wait counting sees (an inline-asm
   // wait is opaque to it, and it then inserts full waits).
@@ -312,10 +314,11 @@ __global__ void __launch_bounds__(512, 1) w8a8_gemm_kernel(const W8GemmArgs a) {
     float s[2];
     load_sx(kb, s);
     __builtin_amdgcn_sched_barrier(0);
-    issue(kb + 2, xnext, wnext);
     const float swk = swp[kb];
     mfma_slot(xbuf, wbuf);
     handover();
+    issue(kb + 2, xnext, wnext);
+    __builtin_amdgcn_sched_barrier(0);
     dequant(part, s, swk);
     end_step();
   };
