@@ -48,6 +48,13 @@
 // Softmax.  Base-2 online softmax with scale*log2(e) folded into one FMA
 // before v_exp_f32.  The running max is raised only when a tile's max
 // exceeds it by more than 8 (so p <= 2^8): the O/l rescale is then rare.
+// The ping-pong kernel goes further in a first, fast pass over a work item:
+// a wave takes the row max only until each of its rows has seen a key, and
+// that first max stays the exp offset.  The offset cancels in O = sum p v /
+// sum p and is added back in the LSE, so any value that keeps p finite gives
+// the same result up to rounding.  A workgroup vote after the pass reruns the
+// item with the lazy rule on every tile if some row sum reached 2^64 or
+// overflowed, i.e. if a later score rose far above the first maximum.
 // Row sums are taken on the bf16-rounded p that feed the PV product: the
 // 4-wave kernel with v_dot2c_f32_bf16 against ones, the ping-pong kernel on
 // the matrix core (a ones operand times P^T, in its matrix phase).
@@ -627,6 +634,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // finite start: the first tile with any visible key always raises it, so -m_run is the exp
   // offset from then on with no test for -inf (a row with no visible key keeps l = 0)
   float m_run[2] = {-1e30f, -1e30f};
+  bool exact = false;  // pass with the row max on every tile (after a failed fast pass)
   // row sums on the matrix core: D (16x16) += ones (16 x 32 keys) . P^T (32 keys x 16 queries)
   // makes every row of D the row sums of the 16 queries, so lane l's lsum[qb] holds the sum of
   // query qb*16 + l%16 (in all four elements)
@@ -751,19 +759,25 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
             }
         }
       }
-      // row max: in-lane over the 16 scores of each query block as three-way maxima, then
-      // across the four lanes that share the query (l16 + {0, 16, 32, 48}), both blocks at once
-      float rmax[2];
+      // Row max.  The exact pass takes it on every tile (lazy rule below).  The fast pass takes
+      // it only until every row of the wave has seen a key: from then on the first max stays
+      // the exp offset (any offset gives the same softmax; this one only has to keep p finite,
+      // which the vote after the pass checks).  A skipped max reads as -inf: no raise.
+      float rmax[2] = {-__builtin_inff(), -__builtin_inff()};
+      if (__builtin_amdgcn_ballot_w64(exact || m_run[0] == -1e30f || m_run[1] == -1e30f) != 0) {
+        // row max: in-lane over the 16 scores of each query block as three-way maxima, then
+        // across the four lanes that share the query (l16 + {0, 16, 32, 48}), both blocks at once
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float m0 = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
-        const float m1 = fmaxf(fmaxf(s[0][qb][3], s[1][qb][0]), s[1][qb][1]);
-        const float m2 = fmaxf(fmaxf(s[1][qb][2], s[1][qb][3]), s[2][qb][0]);
-        const float m3 = fmaxf(fmaxf(s[2][qb][1], s[2][qb][2]), s[2][qb][3]);
-        const float m4 = fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), s[3][qb][2]);
-        rmax[qb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
+        for (int qb = 0; qb < 2; ++qb) {
+          const float m0 = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
+          const float m1 = fmaxf(fmaxf(s[0][qb][3], s[1][qb][0]), s[1][qb][1]);
+          const float m2 = fmaxf(fmaxf(s[1][qb][2], s[1][qb][3]), s[2][qb][0]);
+          const float m3 = fmaxf(fmaxf(s[2][qb][1], s[2][qb][2]), s[2][qb][3]);
+          const float m4 = fmaxf(fmaxf(s[3][qb][0], s[3][qb][1]), s[3][qb][2]);
+          rmax[qb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[3][qb][3]));
+        }
+        rows_max2(rmax[0], rmax[1]);
       }
-      rows_max2(rmax[0], rmax[1]);
       // lazy max update: raised only when a row's max passes m_run + 8 (values stay <= 2^8),
       // tested on the raw scores against (m_run + 8) / c; the update and the O rescale of both
       // query blocks sit in one rare branch
@@ -838,93 +852,114 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  Cur cc, cv, ck;  // mask cursor (tile awaiting softmax); V loads; K loads
-  enter(cc, 0, 0);
-  if (cc.r < nr) {
-    enter(cv, cc.r, 2);
-    Cur k0c, k1c;  // prologue K tiles 0 and 1
-    enter(k0c, cc.r, 1);
-    k1c = k0c;
-    next(k1c, 1);
-    // prologue: K_0 -> kbuf0, V_0 -> vbuf0, K_1 -> kbuf1; S_0 everywhere, softmax of S_0 in
-    // group A (group B takes it in the first pair)
-    if (grp_a) {
-      issue(k0c, false, kbuf0);
-      issue(cv, true, vbuf0);
-      issue(k1c, false, kbuf1);
-    }
-    next(cv, 2);  // now tile 1
-    ck = k1c;
-    next(ck, 1);  // now tile 2
-    publish();
-    auto advance = [&]() {
-      const bool more = cv.r < nr;  // tile j+1 exists (every wave agrees)
-      next(ck, 1);
-      next(cv, 2);
-      return more;
-    };
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-    // Pair j: loads of K_{j+2} and V_{j+1} (by group A, at its matrix phase); the
-    // matrix phase reads K_{j+1} and V_j.  Even pairs read kbuf1 / vbuf0 and load into kbuf0 /
-    // vbuf1, odd pairs the other way round; unrolled by two so the buffers are compile-time
-    // names.  Group A, group B and the waves without rows run separate copies of the loop
-    // (same barriers), so no copy carries another's register assignment.
-    if (!wlive) {
-      __syncthreads();
-      auto pair = [&](char *kw, char *vw) {
-        if (grp_a) {
-          issue(ck, false, kw);
-          issue(cv, true, vw);
-        }
-        const bool more = advance();
-        handover();
-        publish();
+  // One pass over the work item's tiles.  The fast pass runs first; the exact pass runs only
+  // if the fast one let a row sum reach 2^64 or overflow, i.e. a later score far above the
+  // row's first max (p <= 2^(c (max - first max)), l <= that times the key count; inputs of
+  // ordinary scale stay far below).  The exact pass keeps p <= 2^8 by the lazy rule.  The vote
+  // is workgroup-wide, since every wave takes part in the loads and barriers of a pass.  The
+  // lambda is inlined at both calls, so each pass has its own schedule (one loop around a
+  // single copy, with the vote inside it, made the fast pass 12% slower).
+  auto run_pass = [&]() {
+    Cur cc, cv, ck;  // mask cursor (tile awaiting softmax); V loads; K loads
+    enter(cc, 0, 0);
+    if (cc.r < nr) {
+      enter(cv, cc.r, 2);
+      Cur k0c, k1c;  // prologue K tiles 0 and 1
+      enter(k0c, cc.r, 1);
+      k1c = k0c;
+      next(k1c, 1);
+      // prologue: K_0 -> kbuf0, V_0 -> vbuf0, K_1 -> kbuf1; S_0 everywhere, softmax of S_0 in
+      // group A (group B takes it in the first pair)
+      if (grp_a) {
+        issue(k0c, false, kbuf0);
+        issue(cv, true, vbuf0);
+        issue(k1c, false, kbuf1);
+      }
+      next(cv, 2);  // now tile 1
+      ck = k1c;
+      next(ck, 1);  // now tile 2
+      publish();
+      auto advance = [&]() {
+        const bool more = cv.r < nr;  // tile j+1 exists (every wave agrees)
+        next(ck, 1);
+        next(cv, 2);
         return more;
       };
-      while (pair(kbuf0, vbuf1) && pair(kbuf1, vbuf0)) {
-      }
-    } else {
-      {
-        const lds_char *K0 = (const lds_char *)kbuf0;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) qk_step(K0, kb, ks);
-      }
-      if (grp_a) {
-        softmax_phase(cc);
-        __syncthreads();  // every wave has read kbuf0 before the first pair loads K_2 into it
-        auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
-          matrix_phase(kr, vr, yes{}, ck, kw, cv, vw);
-          pin_matrix();
+      using yes = std::integral_constant<bool, true>;
+      using no = std::integral_constant<bool, false>;
+      // Pair j: loads of K_{j+2} and V_{j+1} (by group A, at its matrix phase); the
+      // matrix phase reads K_{j+1} and V_j.  Even pairs read kbuf1 / vbuf0 and load into kbuf0 /
+      // vbuf1, odd pairs the other way round; unrolled by two so the buffers are compile-time
+      // names.  Group A, group B and the waves without rows run separate copies of the loop
+      // (same barriers), so no copy carries another's register assignment.
+      if (!wlive) {
+        __syncthreads();
+        auto pair = [&](char *kw, char *vw) {
+          if (grp_a) {
+            issue(ck, false, kw);
+            issue(cv, true, vw);
+          }
           const bool more = advance();
           handover();
-          if (more) {
-            softmax_phase(cc);
-            pin_softmax();
-          }
           publish();
           return more;
         };
-        while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+        while (pair(kbuf0, vbuf1) && pair(kbuf1, vbuf0)) {
         }
       } else {
-        __syncthreads();
-        auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
-          const bool more = advance();
+        {
+          const lds_char *K0 = (const lds_char *)kbuf0;
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+  #pragma unroll
+            for (int kb = 0; kb < 4; ++kb) qk_step(K0, kb, ks);
+        }
+        if (grp_a) {
           softmax_phase(cc);
-          pin_softmax();
-          handover();
-          matrix_phase(kr, vr, no{}, ck, kw, cv, vw);
-          pin_matrix();
-          publish();
-          return more;
-        };
-        while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+          __syncthreads();  // every wave has read kbuf0 before the first pair loads K_2 into it
+          auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
+            matrix_phase(kr, vr, yes{}, ck, kw, cv, vw);
+            pin_matrix();
+            const bool more = advance();
+            handover();
+            if (more) {
+              softmax_phase(cc);
+              pin_softmax();
+            }
+            publish();
+            return more;
+          };
+          while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+          }
+        } else {
+          __syncthreads();
+          auto pair = [&](const char *kr, const char *vr, char *kw, char *vw) {
+            const bool more = advance();
+            softmax_phase(cc);
+            pin_softmax();
+            handover();
+            matrix_phase(kr, vr, no{}, ck, kw, cv, vw);
+            pin_matrix();
+            publish();
+            return more;
+          };
+          while (pair(kbuf1, vbuf0, kbuf0, vbuf1) && pair(kbuf0, vbuf1, kbuf1, vbuf0)) {
+          }
         }
       }
     }
+  };
+  run_pass();
+  bool bad = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) bad = bad || !(lsum[qb][0] < 0x1p64f);
+  if (__syncthreads_or(bad)) {
+    exact = true;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) oacc[cb][0] = oacc[cb][1] = f32x4_t{};
+    m_run[0] = m_run[1] = -1e30f;
+    lsum[0] = lsum[1] = f32x4_t{};
+    run_pass();
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.  A query's row sum is spread over

@@ -1,10 +1,15 @@
 """Degenerate and ragged calls on the GPU against the oracle, through both bf16 kernels
 (128-row work items and the 256-row ping-pong kernel): no query rows at all, a reference image
 with no tokens, one-token frames, a single query row, reference rows only, head_dim 64 with
-ragged frame sizes."""
+ragged frame sizes, and rows whose scores spread so far that the ping-pong kernel's fast pass
+hands the work item to its exact pass."""
+import numpy as np
 import pytest
 
+import fa_workloads as W
 import gpu_helpers as G
+from frame_aligned_attention_amd import binding as B
+from gpu_helpers import random_call
 
 pytestmark = pytest.mark.gpu
 
@@ -54,3 +59,50 @@ def test_head_dim_64_ragged(br):
     G.say("case: head_dim 64, 333-token frames, block_rows %d" % br)
     c = G.random_call(36, 333, 2, 2, 64, ref_tokens=[45], ref_t0=[1], block_rows=br)
     G.compare_all(c, G.run_call(c), "hd64 ragged")
+
+
+def _score_spread_call(seed, a, br, key_split):
+    """Scores far apart within every row: q = a*u + noise, the first 64 keys of every frame of
+    the chunk and the source and of the reference image k = -a*u + noise, all other keys
+    k = a*u + noise (u a random sign vector), so each row's first tile scores about -128 a^2
+    and later tiles +128 a^2."""
+    T, C, H, D = 192, 2, 2, 128
+    c = random_call(seed, T, C, H, D, ref_tokens=[128], ref_t0=[0], block_rows=br,
+                    key_split=key_split)
+    g = np.random.default_rng(seed + 1)
+    u = np.where(g.random((H, D)) < 0.5, -1.0, 1.0).astype(np.float32)
+    noise = lambda x: W.round_bf16(a * u + 0.5 * x)
+
+    def keys(k, frame_len):
+        pos = np.arange(k.shape[0]) % frame_len
+        out = noise(k)
+        low = pos < 64
+        out[low] = W.round_bf16(-a * u + 0.5 * k[low])
+        return out
+
+    for kind in c.q:
+        c.q[kind] = noise(c.q[kind])
+    c.k_hist = keys(c.k_hist, T)
+    c.k_src = keys(c.k_src, T)
+    c.k_ref = keys(c.k_ref, 128)
+    return c
+
+
+@BR
+@pytest.mark.parametrize("a", [2.0, 1.5], ids=["overflow", "sum2e64"])
+def test_score_spread_exact_pass(br, a):
+    """A row whose first tile scores ~c*256 a^2 (log2 units) below its later tiles: with a = 2
+    the ping-pong kernel's fast pass, whose exp offset is the first tile's max, overflows
+    (p ~ 2^130) and with a = 1.5 its row sums pass 2^64; either way the workgroup vote reruns the
+    item with the row max on every tile.  Compared with the oracle like any call (key split off,
+    so every item's first tile is a low one)."""
+    G.say("case: score spread a=%g, block_rows %d" % (a, br))
+    c = _score_spread_call(41, a, br, B.FA_KEY_SPLIT_OFF)
+    res = G.run_call(c)
+    ref = G.oracle_all(c)
+    for k, (o, lse) in res.items():
+        assert np.isfinite(o).all() and np.isfinite(lse).all(), k
+        # a handful of keys carry each row's mass (their scores spread over ~10 in log2
+        # units), so the LSE bound is the one-key cap (count 1), not the N(0,1) one
+        G.tol_check(o, ref[k][0], "bf16", "score spread a=%g %s rows" % (a, G.KIND_NAMES[k]),
+                    lse, ref[k][1], counts=np.ones((1, lse.shape[1])))
