@@ -635,6 +635,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // offset from then on with no test for -inf (a row with no visible key keeps l = 0)
   float m_run[2] = {-1e30f, -1e30f};
   bool exact = false;  // pass with the row max on every tile (after a failed fast pass)
+  bool seeded = false;  // fast pass: every row of the wave has seen a key (wave-uniform)
   // row sums on the matrix core: D (16x16) += ones (16 x 32 keys) . P^T (32 keys x 16 queries)
   // makes every row of D the row sums of the 16 queries, so lane l's lsum[qb] holds the sum of
   // query qb*16 + l%16 (in all four elements)
@@ -759,12 +760,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
             }
         }
       }
-      // Row max.  The exact pass takes it on every tile (lazy rule below).  The fast pass takes
-      // it only until every row of the wave has seen a key: from then on the first max stays
-      // the exp offset (any offset gives the same softmax; this one only has to keep p finite,
-      // which the vote after the pass checks).  A skipped max reads as -inf: no raise.
+      // Row max and lazy test.  The exact pass takes them on every tile.  The fast pass takes
+      // them only until every row of the wave has seen a key (`seeded`, a wave-uniform flag):
+      // from then on the first max stays the exp offset (any offset gives the same softmax;
+      // this one only has to keep p finite, which the vote after the pass checks).
       float rmax[2] = {-__builtin_inff(), -__builtin_inff()};
-      if (__builtin_amdgcn_ballot_w64(exact || m_run[0] == -1e30f || m_run[1] == -1e30f) != 0) {
+      if (exact || !seeded) {
         // row max: in-lane over the 16 scores of each query block as three-way maxima, then
         // across the four lanes that share the query (l16 + {0, 16, 32, 48}), both blocks at once
 #pragma unroll
@@ -780,8 +781,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
       }
       // lazy max update: raised only when a row's max passes m_run + 8 (values stay <= 2^8),
       // tested on the raw scores against (m_run + 8) / c; the update and the O rescale of both
-      // query blocks sit in one rare branch
-      {
+      // query blocks sit in one rare branch (a separate branch on the same flag: inside the
+      // row-max branch the kernel spilled)
+      if (exact || !seeded) {
         const bool need0 = rmax[0] > fmaf(m_run[0], cinv, kThr * cinv);
         const bool need1 = rmax[1] > fmaf(m_run[1], cinv, kThr * cinv);
         if (__builtin_amdgcn_ballot_w64(need0 || need1) != 0) {
@@ -797,6 +799,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
           }
         }
       }
+      if (!exact && !seeded)
+        seeded = __builtin_amdgcn_ballot_w64(m_run[0] == -1e30f || m_run[1] == -1e30f) == 0;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float mneg = -m_run[qb];
@@ -860,6 +864,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(const AttnArgs a) 
   // lambda is inlined at both calls, so each pass has its own schedule (one loop around a
   // single copy, with the vote inside it, made the fast pass 12% slower).
   auto run_pass = [&]() {
+    seeded = false;
     Cur cc, cv, ck;  // mask cursor (tile awaiting softmax); V loads; K loads
     enter(cc, 0, 0);
     if (cc.r < nr) {
