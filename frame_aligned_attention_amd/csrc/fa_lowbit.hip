@@ -2,6 +2,9 @@
 // quantiser (per-head key mean, per-128-token-block int8 Q/K and e4m3 V) and the
 // attention kernel with int8 Q.K^T (v_mfma_i32_32x32x32_i8) and e4m3 P.V
 // (v_mfma_scale_f32_32x32x64_f8f6f4), fp32 online softmax.
+// build-flags: -fno-honor-nans
+// (Finite inputs give no NaN here; without the flag every row max first quiets the
+// scores it compares, 4 more VALU instructions per tile.)
 //
 // The pages name low-bit attention only ("Vidu S2" launch article, technical
 // stack section; tech report, hybrid-attention paragraph).  What it computes here:
@@ -261,16 +264,20 @@ __device__ __forceinline__ int sw(int r) { return ((r >> 2) & 1) | (r & 2) | ((r
 //    to float conversion is needed; kBias * fk is folded into the exp FMA (that term rounds
 //    once per tile, to under one unit of the integer score, far below the int8 rounding of q.k);
 //  - V block scales are powers of two, applied by the PV MFMA's own e8m0 block scale, so every
-//    tile takes p' = p * 2^(8 - kThr) with no per-tile weight;
+//    tile takes p' = p * 2^8 with no per-tile weight;
 //  - the row sums of p' come from a 16x16x128 e4m3 MFMA of a ones pattern against P^T (the same
 //    e4m3 values the PV product uses), not from 32 adds.
-// The running max is exact (kThr = 0): a lazy one (p up to 4) cost accuracy on small rows.
+// The running max is raised only when a row's max passes it by more than kThr = 0.75, so p' stays
+// below 2^8.75 ~ 430, under e4m3's 448, and most tiles past the first skip the rescale (with an
+// exact max some row of the wave sets a new one on a large share of tiles).  Values only get
+// larger than under the exact max, never closer to e4m3's subnormals; a lazier max with a
+// smaller shift (p' = p 2^6, raised past +2) cost accuracy on small rows.
 __global__ void __launch_bounds__(256, 2) attn_lowbit_kernel(const AttnArgs a) {
   using namespace lb;
   constexpr int kBiasBits = 0x4B400000;
   constexpr float kBias = 12582912.0f;
-  constexpr float kThr = 0.0f;
-  constexpr float kPShift = 8.0f - kThr;  // p' = p * 2^kPShift <= 256
+  constexpr float kThr = 0.75f;
+  constexpr float kPShift = 8.0f;  // p' = p * 2^kPShift < 2^(8 + kThr) ~ 430 < 448
   __shared__ __attribute__((aligned(1024))) char kbuf0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kbuf1[TILEB];
   __shared__ __attribute__((aligned(1024))) char vbuf0[TILEB];
