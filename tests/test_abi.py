@@ -222,8 +222,11 @@ def test_w8a8_gemm_argument_checks():
 
 def test_per_source_build_flags():
     """A source's `// build-flags:` line is what the build passes for it (and it sits in the
-    hashed source text); only the bf16 attention file asks for any."""
+    hashed source text); only the two attention files with row maxima ask for any (no NaN
+    quieting before the maxima)."""
     from frame_aligned_attention_amd import build as fb
     flags = {os.path.basename(s): fb.file_flags(s) for s in fb.sources()}
-    assert flags["fa_attn_bf16.hip"] == ["-fno-honor-nans"]
-    assert all(v == [] for k, v in flags.items() if k != "fa_attn_bf16.hip")
+    with_flags = ("fa_attn_bf16.hip", "fa_lowbit.hip")
+    for k in with_flags:
+        assert flags[k] == ["-fno-honor-nans"], k
+    assert all(v == [] for k, v in flags.items() if k not in with_flags)
